@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Throughput of direct all-pairs softened gravity on one MI355X.
+
+One step = one kick-drift-kick leapfrog step of the whole body set:
+nbody_leapfrog_step (kick + drift), nbody_accel (the O(N^2) force pass) and
+nbody_kick (closing half-kick).  The default workload is the N = 1,048,576
+Plummer sphere (equal masses 1/N, eps^2 = 1e-4, dt = 1e-4).  value = N^2
+body-body interactions per step / seconds per step, in billions per second.
+
+Inputs are resident in HBM before the timed region; the region is bracketed by
+torch.cuda.synchronize() on both sides.  The force kernel's own duration is
+measured with HIP events recorded on the stream it is launched on (the current
+torch stream) around every launch; the roofline object reports it against the
+MI355X FP32 vector peak at 20 flops per interaction (the count of
+"Cuda Nbody Notes").
+
+The energy / momentum pass (a checkpoint diagnostic, not part of a step) is
+timed separately.  The CPU baseline is the double-precision oracle timed on a
+bounded sample of the same workload's rows on the host cores.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FLOPS_PER_INTERACTION = 20          # "Cuda Nbody Notes", pair-step comments
+PEAK_FP32_TFLOPS = 157.3            # MI355X FP32 vector, 256 CU x 64 lanes x 2 x 2 x 2.4 GHz
+METRIC = "body-body interactions/s (billions), N=1M fp32; % of MI355X FP32 VALU peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "force_plummer1m_traffic.json")
+KERNEL_SOURCES = ("direct_all_pairs_softened_amd/csrc/force.hip",
+                  "direct_all_pairs_softened_amd/csrc/nbody_common.hpp")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_per_launch():
+    """HBM bytes per force launch from the committed counter summary, or None
+    when it is missing or was taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(pm_np, acc0_np, w, seconds):
+    """The oracle, untuned, on a bounded sample of rows: each row is the full
+    N-term double-precision sum.  Returns the JSON object."""
+    import numpy as np
+    import oracle
+    pos, mass = oracle.split_posmass(pm_np)
+    G, eps2 = float(np.float32(w.G)), float(np.float32(w.eps2))
+    g = np.random.default_rng(123)
+    probe = np.sort(g.choice(w.n, 64, replace=False))
+    t0 = time.perf_counter()
+    oracle.accel_rows(pos, mass, G, eps2, probe)
+    rate = 64 / max(time.perf_counter() - t0, 1e-6)
+    rows = int(min(w.n, max(64, rate * seconds)))
+    sample = np.sort(g.choice(w.n, rows, replace=False))
+    t0 = time.perf_counter()
+    ref = oracle.accel_rows(pos, mass, G, eps2, sample)
+    dt = time.perf_counter() - t0
+    got = acc0_np[sample, :3].astype(np.float64)
+    l2 = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    per = float((np.linalg.norm(got - ref, axis=1) / np.linalg.norm(ref, axis=1)).max())
+    inter = rows * w.n
+    return {
+        "value": inter / dt / 1e9,
+        "unit": "billion interactions/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{rows} of {w.n} bodies, each summed over all {w.n} (float64, "
+                  f"{inter:.3e} interactions in {dt:.1f} s)",
+        "sample_parity_vs_gpu": {"rel_l2": l2, "worst_body_rel": per},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="plummer1m")
+    ap.add_argument("--variant", type=int, default=None, help="force a compiled force variant")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target length of the oracle CPU-baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(the force pass would shard by i with an all-gather of positions).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import direct_all_pairs_softened_amd as nb
+    import workloads
+
+    nb.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = workloads.WORKLOADS[args.workload]
+    dt = w.dt if w.dt > 0 else 1e-4
+    log(f"workload {w.name}: {w.description}")
+    pm_np, vel_np = workloads.make(w.name)
+    dev = torch.device("cuda:0")
+    pm = torch.from_numpy(pm_np).to(dev)
+    vel = torch.from_numpy(vel_np).to(dev)
+    acc = torch.empty_like(pm)
+    variant = args.variant if args.variant is not None else nb.nbody_accel_variant_for_n(w.n)
+    info = nb.nbody_accel_variant_info(variant)
+
+    def force():
+        nb.nbody_accel_variant(pm, w.G, w.eps2, acc, variant)
+
+    force()
+    torch.cuda.synchronize()
+    acc0_np = acc.cpu().numpy()
+
+    def step():
+        nb.nbody_leapfrog_step(pm, vel, acc, dt)
+        force()
+        nb.nbody_kick(vel, acc, 0.5 * dt)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        nb.nbody_leapfrog_step(pm, vel, acc, dt)
+        ev[k][0].record(stream)
+        force()
+        ev[k][1].record(stream)
+        nb.nbody_kick(vel, acc, 0.5 * dt)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    force_ms = [a.elapsed_time(b) for a, b in ev]
+    force_avg = sum(force_ms) / len(force_ms)
+    inter = float(w.n) * float(w.n)
+    value = inter / (ms_per_step * 1e-3) / 1e9
+    achieved = FLOPS_PER_INTERACTION * inter / (force_avg * 1e-3) / 1e12
+    log(f"step {ms_per_step:.3f} ms, force kernel {force_avg:.3f} ms "
+        f"(min {min(force_ms):.3f}), {value:.1f} G interactions/s per step")
+
+    # energy diagnostic (outside the timed steps)
+    ws = torch.empty(nb.nbody_energy_workspace_bytes(w.n), dtype=torch.uint8, device=dev)
+    stats = torch.zeros(8, dtype=torch.float64, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    nb.nbody_energy(pm, vel, w.G, w.eps2, ws, stats)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    energy_ms = e0.elapsed_time(e1)
+
+    traffic = traffic_per_launch()
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "billion interactions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "n": w.n,
+            "bodies": w.description,
+            "eps2": w.eps2,
+            "G": w.G,
+            "dt": dt,
+            "step": "kick+drift, force pass, half-kick",
+            "force_variant": variant,
+            "force_tiling": info,
+        },
+        "pct_fp32_peak": 100.0 * achieved / PEAK_FP32_TFLOPS,
+        "force_ms": force_avg,
+        "energy_ms": energy_ms,
+        "roofline": {
+            "bound": "alu",
+            "achieved": achieved,
+            "peak": PEAK_FP32_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_FP32_TFLOPS,
+            "traffic": traffic,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline: timing the oracle on a row sample ...")
+        out["cpu_baseline"] = cpu_baseline(pm_np, acc0_np, w, args.cpu_seconds)
+        log(f"cpu baseline: {out['cpu_baseline']['value']:.3f} G interactions/s on "
+            f"{out['cpu_baseline']['cores']} threads")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,230 @@
+// C ABI of libnbody.so (declared in include/nbody.h): argument validation and
+// dispatch to the kernel launchers.  Every check runs before anything is
+// enqueued, and none of them touches device memory or the HIP runtime, so
+// invalid calls fail the same way with or without a GPU.
+#include "nbody.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "nbody_internal.hpp"
+
+namespace {
+
+using nbody::BodyArrays;
+using nbody::Layout;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// [a, a + na) and [b, b + nb) share at least one byte.
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na && nb && x < y + nb && y < x + na;
+}
+
+bool n_ok(int64_t n) { return n >= 0 && n <= NBODY_MAX_N; }
+
+int check_consts(float G, float eps2) {
+  if (!isfinite(G) || !isfinite(eps2) || !(eps2 > 0.0f)) return NBODY_ERR_INVALID_ARG;
+  return NBODY_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? NBODY_OK : NBODY_ERR_HIP; }
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+int force_aos4(const float *posmass, int64_t n, float G, float eps2, float *accel_out,
+               int variant, void *stream) {
+  if (!n_ok(n)) return NBODY_ERR_INVALID_ARG;
+  if (int s = check_consts(G, eps2)) return s;
+  if (!nbody::force_variant(variant)) return NBODY_ERR_INVALID_ARG;
+  if (n == 0) return NBODY_OK;
+  if (!posmass || !accel_out) return NBODY_ERR_INVALID_ARG;
+  if (!aligned(posmass, 16) || !aligned(accel_out, 16)) return NBODY_ERR_ALIGNMENT;
+  const size_t bytes = (size_t)n * 16;
+  if (overlap(posmass, bytes, accel_out, bytes)) return NBODY_ERR_ALIAS;
+  BodyArrays b;
+  b.posmass = posmass;
+  b.accel4 = accel_out;
+  return hip_status(nbody::launch_force(variant, Layout::Aos4, b, (int)n, G, eps2,
+                                        as_stream(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *nbody_status_string(int status) {
+  switch (status) {
+    case NBODY_OK:
+      return "ok";
+    case NBODY_ERR_INVALID_ARG:
+      return "invalid argument (null pointer, body count out of range, eps2 <= 0 or a "
+             "non-finite constant, unknown variant or bad split size)";
+    case NBODY_ERR_ALIGNMENT:
+      return "misaligned array (float4 arrays need 16 bytes, float arrays 4)";
+    case NBODY_ERR_ALIAS:
+      return "an output array overlaps an array it must not";
+    case NBODY_ERR_WORKSPACE:
+      return "workspace missing or too small";
+    case NBODY_ERR_HIP:
+      return "HIP launch or runtime error";
+    default:
+      return "unknown status";
+  }
+}
+
+int nbody_abi_version(void) { return NBODY_ABI_VERSION; }
+
+int nbody_accel_variant_count(void) { return nbody::force_variant_count(); }
+
+int nbody_accel_variant_info(int v, int *bodies_per_lane, int *tile, int *waves_per_block,
+                             int *split) {
+  const nbody::ForceVariant *fv = nbody::force_variant(v);
+  if (!fv) return NBODY_ERR_INVALID_ARG;
+  if (bodies_per_lane) *bodies_per_lane = fv->bodies_per_lane;
+  if (tile) *tile = fv->tile;
+  if (waves_per_block) *waves_per_block = fv->waves;
+  if (split) *split = fv->split;
+  return NBODY_OK;
+}
+
+int nbody_accel_variant_for_n(int64_t n) { return nbody::force_variant_for_n(n); }
+
+int nbody_accel(const float *posmass, int64_t n, float G, float eps2, float *accel_out,
+                void *stream) {
+  return force_aos4(posmass, n, G, eps2, accel_out, nbody::force_variant_for_n(n), stream);
+}
+
+int nbody_accel_variant(const float *posmass, int64_t n, float G, float eps2, float *accel_out,
+                        int variant, void *stream) {
+  return force_aos4(posmass, n, G, eps2, accel_out, variant, stream);
+}
+
+int nbody_accel_f3aos(const float *pos, const float *mass, int64_t n, float G, float eps2,
+                      float *accel_out, void *stream) {
+  if (!n_ok(n)) return NBODY_ERR_INVALID_ARG;
+  if (int s = check_consts(G, eps2)) return s;
+  if (n == 0) return NBODY_OK;
+  if (!pos || !mass || !accel_out) return NBODY_ERR_INVALID_ARG;
+  if (!aligned(pos, 4) || !aligned(mass, 4) || !aligned(accel_out, 4)) return NBODY_ERR_ALIGNMENT;
+  const size_t b3 = (size_t)n * 12, b1 = (size_t)n * 4;
+  if (overlap(accel_out, b3, pos, b3) || overlap(accel_out, b3, mass, b1)) return NBODY_ERR_ALIAS;
+  BodyArrays b;
+  b.pos3 = pos;
+  b.mass = mass;
+  b.accel3 = accel_out;
+  return hip_status(nbody::launch_force(nbody::force_variant_for_n(n), Layout::Aos3, b, (int)n,
+                                        G, eps2, as_stream(stream)));
+}
+
+int nbody_accel_soa(const float *x, const float *y, const float *z, const float *m, int64_t n,
+                    float G, float eps2, float *ax, float *ay, float *az, void *stream) {
+  if (!n_ok(n)) return NBODY_ERR_INVALID_ARG;
+  if (int s = check_consts(G, eps2)) return s;
+  if (n == 0) return NBODY_OK;
+  const float *in[4] = {x, y, z, m};
+  float *out[3] = {ax, ay, az};
+  for (const float *p : in)
+    if (!p) return NBODY_ERR_INVALID_ARG;
+  for (const float *p : out)
+    if (!p) return NBODY_ERR_INVALID_ARG;
+  for (const float *p : in)
+    if (!aligned(p, 4)) return NBODY_ERR_ALIGNMENT;
+  for (const float *p : out)
+    if (!aligned(p, 4)) return NBODY_ERR_ALIGNMENT;
+  const size_t b1 = (size_t)n * 4;
+  for (int o = 0; o < 3; ++o) {
+    for (const float *p : in)
+      if (overlap(out[o], b1, p, b1)) return NBODY_ERR_ALIAS;
+    for (int o2 = o + 1; o2 < 3; ++o2)
+      if (overlap(out[o], b1, out[o2], b1)) return NBODY_ERR_ALIAS;
+  }
+  BodyArrays b;
+  b.x = x;
+  b.y = y;
+  b.z = z;
+  b.m = m;
+  b.ax = ax;
+  b.ay = ay;
+  b.az = az;
+  return hip_status(nbody::launch_force(nbody::force_variant_for_n(n), Layout::Soa, b, (int)n, G,
+                                        eps2, as_stream(stream)));
+}
+
+size_t nbody_accel_splitj_workspace_bytes(int64_t n, int64_t j_chunk) {
+  if (!n_ok(n)) return 0;
+  return nbody::splitj_workspace_bytes(n, j_chunk);
+}
+
+int nbody_accel_splitj(const float *posmass, int64_t n, float G, float eps2, float *accel_out,
+                       int64_t j_chunk, void *workspace, size_t workspace_bytes, void *stream) {
+  if (!n_ok(n)) return NBODY_ERR_INVALID_ARG;
+  if (int s = check_consts(G, eps2)) return s;
+  if (j_chunk < 32 || j_chunk % 32 != 0 || j_chunk > NBODY_MAX_N) return NBODY_ERR_INVALID_ARG;
+  if (n == 0) return NBODY_OK;
+  // the chunk index is the grid's y dimension
+  if ((n + j_chunk - 1) / j_chunk > 65535) return NBODY_ERR_INVALID_ARG;
+  if (!posmass || !accel_out) return NBODY_ERR_INVALID_ARG;
+  if (!aligned(posmass, 16) || !aligned(accel_out, 16)) return NBODY_ERR_ALIGNMENT;
+  const size_t need = nbody::splitj_workspace_bytes(n, j_chunk);
+  if (!workspace || workspace_bytes < need) return NBODY_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return NBODY_ERR_ALIGNMENT;
+  const size_t bytes = (size_t)n * 16;
+  if (overlap(posmass, bytes, accel_out, bytes) || overlap(workspace, need, posmass, bytes) ||
+      overlap(workspace, need, accel_out, bytes))
+    return NBODY_ERR_ALIAS;
+  return hip_status(nbody::launch_splitj(posmass, (int)n, G, eps2, accel_out, (int)j_chunk,
+                                         workspace, as_stream(stream)));
+}
+
+int nbody_leapfrog_step(float *posmass, float *vel, const float *accel, float dt, int64_t n,
+                        void *stream) {
+  if (!n_ok(n) || !isfinite(dt)) return NBODY_ERR_INVALID_ARG;
+  if (n == 0) return NBODY_OK;
+  if (!posmass || !vel || !accel) return NBODY_ERR_INVALID_ARG;
+  if (!aligned(posmass, 16) || !aligned(vel, 16) || !aligned(accel, 16))
+    return NBODY_ERR_ALIGNMENT;
+  const size_t bytes = (size_t)n * 16;
+  if (overlap(posmass, bytes, vel, bytes) || overlap(posmass, bytes, accel, bytes) ||
+      overlap(vel, bytes, accel, bytes))
+    return NBODY_ERR_ALIAS;
+  return hip_status(nbody::launch_leapfrog(posmass, vel, accel, dt, (int)n, as_stream(stream)));
+}
+
+int nbody_kick(float *vel, const float *accel, float h, int64_t n, void *stream) {
+  if (!n_ok(n) || !isfinite(h)) return NBODY_ERR_INVALID_ARG;
+  if (n == 0) return NBODY_OK;
+  if (!vel || !accel) return NBODY_ERR_INVALID_ARG;
+  if (!aligned(vel, 16) || !aligned(accel, 16)) return NBODY_ERR_ALIGNMENT;
+  const size_t bytes = (size_t)n * 16;
+  if (overlap(vel, bytes, accel, bytes)) return NBODY_ERR_ALIAS;
+  return hip_status(nbody::launch_kick(vel, accel, h, (int)n, as_stream(stream)));
+}
+
+size_t nbody_energy_workspace_bytes(int64_t n) {
+  if (!n_ok(n)) return 0;
+  return nbody::energy_workspace_bytes(n);
+}
+
+int nbody_energy(const float *posmass, const float *vel, int64_t n, float G, float eps2,
+                 void *workspace, size_t workspace_bytes, double *stats_out, void *stream) {
+  if (!n_ok(n)) return NBODY_ERR_INVALID_ARG;
+  if (int s = check_consts(G, eps2)) return s;
+  if (n == 0) return NBODY_OK;  // stats_out is left untouched
+  if (!posmass || !vel || !stats_out) return NBODY_ERR_INVALID_ARG;
+  if (!aligned(stats_out, 8)) return NBODY_ERR_ALIGNMENT;
+  if (!aligned(posmass, 16) || !aligned(vel, 16)) return NBODY_ERR_ALIGNMENT;
+  const size_t need = nbody::energy_workspace_bytes(n);
+  if (!workspace || workspace_bytes < need) return NBODY_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return NBODY_ERR_ALIGNMENT;
+  const size_t bytes = (size_t)n * 16, sb = 8 * sizeof(double);
+  if (overlap(workspace, need, posmass, bytes) || overlap(workspace, need, vel, bytes) ||
+      overlap(workspace, need, stats_out, sb) || overlap(stats_out, sb, posmass, bytes) ||
+      overlap(stats_out, sb, vel, bytes))
+    return NBODY_ERR_ALIAS;
+  return hip_status(nbody::launch_energy(posmass, vel, (int)n, G, eps2, workspace, stats_out,
+                                         as_stream(stream)));
+}
+
+}  // extern "C"

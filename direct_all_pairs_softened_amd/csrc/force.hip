@@ -1,0 +1,237 @@
+// Force pass: LDS-tiled all-pairs softened gravity for gfx950.
+//
+// Decomposition (the tiled scheme of "Cuda Nbody Notes" and of section 3.1
+// of the "CUDA N-Body Simulation" README, rebuilt for 64-wide wavefronts):
+//  - each lane keeps K i-bodies and their accumulators in VGPRs;
+//  - a block of `waves` wavefronts stages j-bodies in LDS tiles of T bodies;
+//    every lane of a wave reads the same LDS address, which the LDS serves as
+//    a broadcast (the CUDA Handbook's shared-memory page makes the same point
+//    for warps);
+//  - the block may split j over S parts (waves / S waves per part): each part
+//    walks its own contiguous range of tiles and the part sums are added in
+//    ascending part order through LDS at the end.  This keeps small n
+//    occupying the chip without a global workspace or atomics;
+//  - tiles are double-buffered: the next tile's global loads are issued
+//    before the current tile's arithmetic and written to the other LDS buffer
+//    after it, so there is one barrier per tile;
+//  - ragged n: staged indices are clamped into [0, n) and the mass of every
+//    padding slot is zeroed, so the inner loop has no bounds test and a
+//    padding term adds exactly +0 (README section 3.1 guards the same tail
+//    with a loop bound instead).
+// No MFMA: the pair step is a reciprocal square root and a handful of
+// multiply-adds per pair, not a dense contraction.
+#include "nbody_common.hpp"
+#include "nbody_internal.hpp"
+
+namespace nbody {
+
+template <int K, int T, int WAVES, int S, int U, class L>
+__global__ __launch_bounds__(WAVES *kWave) void force_tile_kernel(L lay, int n, int n_tiles,
+                                                                  int tiles_per_part, float G,
+                                                                  float eps2) {
+  constexpr int GW = WAVES / S;            // i-groups (waves) per part
+  constexpr int NTHREADS = WAVES * kWave;  // threads per block
+  constexpr int LOADS = (S * T) / NTHREADS;
+  static_assert(WAVES % S == 0, "waves must be a multiple of the split");
+  static_assert((S * T) % NTHREADS == 0, "staged bodies must divide evenly over threads");
+  static_assert((S - 1) * GW * K * 3 * kWave <= 2 * S * T * 4,
+                "part-combine scratch must fit in the tile buffers");
+  __shared__ float4 tile[2][S * T];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
+  const int part = wave / GW;
+  const int grp = wave % GW;
+  const int base = blockIdx.x * (GW * kWave * K) + grp * kWave + lane;
+
+  float xi[K], yi[K], zi[K], ax[K], ay[K], az[K];
+#pragma unroll
+  for (int q = 0; q < K; ++q) {
+    const int i = base + q * GW * kWave;
+    const float4 b = lay.load(i < n ? i : n - 1);
+    xi[q] = b.x;
+    yi[q] = b.y;
+    zi[q] = b.z;
+    ax[q] = 0.0f;
+    ay[q] = 0.0f;
+    az[q] = 0.0f;
+  }
+
+  // Staging slot e of a step holds body jj = e % T of part e / T's tile.
+  // The padding test is kept apart from the load and applied in stash(), so
+  // the global load stays in flight across the current tile's arithmetic.
+  float4 reg[LOADS];
+  bool real[LOADS];
+  auto fetch = [&](int step) {
+#pragma unroll
+    for (int r = 0; r < LOADS; ++r) {
+      const int e = tid + r * NTHREADS;
+      const int j = ((e / T) * tiles_per_part + step) * T + (e % T);
+      reg[r] = lay.load(j < n ? j : n - 1);
+      real[r] = j < n;
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < LOADS; ++r) {
+      float4 b = reg[r];
+      b.w = real[r] ? b.w : 0.0f;
+      tile[buf][tid + r * NTHREADS] = b;
+    }
+  };
+
+  fetch(0);
+  stash(0);
+  for (int step = 0; step < tiles_per_part; ++step) {
+    __syncthreads();
+    const int cur = step & 1;
+    const bool more = step + 1 < tiles_per_part;
+    if (more) fetch(step + 1);
+    if (part * tiles_per_part + step < n_tiles) {
+      const float4 *tp = &tile[cur][part * T];
+      float px[K], py[K], pz[K];
+#pragma unroll
+      for (int q = 0; q < K; ++q) {
+        px[q] = 0.0f;
+        py[q] = 0.0f;
+        pz[q] = 0.0f;
+      }
+#pragma unroll U
+      for (int jj = 0; jj < T; ++jj) {
+        const float4 b = tp[jj];
+#pragma unroll
+        for (int q = 0; q < K; ++q)
+          pair_accel(b.x, b.y, b.z, b.w, xi[q], yi[q], zi[q], eps2, px[q], py[q], pz[q]);
+      }
+#pragma unroll
+      for (int q = 0; q < K; ++q) {
+        ax[q] += px[q];
+        ay[q] += py[q];
+        az[q] += pz[q];
+      }
+    }
+    if (more) stash(cur ^ 1);
+  }
+
+  if constexpr (S > 1) {
+    __syncthreads();  // every wave is done with the tiles; reuse them
+    float *red = reinterpret_cast<float *>(&tile[0][0]);
+    if (part > 0) {
+#pragma unroll
+      for (int q = 0; q < K; ++q) {
+        const int o = ((((part - 1) * GW + grp) * K + q) * 3) * kWave + lane;
+        red[o] = ax[q];
+        red[o + kWave] = ay[q];
+        red[o + 2 * kWave] = az[q];
+      }
+    }
+    __syncthreads();
+    if (part == 0) {
+      for (int p = 1; p < S; ++p) {
+#pragma unroll
+        for (int q = 0; q < K; ++q) {
+          const int o = ((((p - 1) * GW + grp) * K + q) * 3) * kWave + lane;
+          ax[q] += red[o];
+          ay[q] += red[o + kWave];
+          az[q] += red[o + 2 * kWave];
+        }
+      }
+    }
+  }
+
+  if (part == 0) {
+#pragma unroll
+    for (int q = 0; q < K; ++q) {
+      const int i = base + q * GW * kWave;
+      if (i < n) lay.store(i, G * ax[q], G * ay[q], G * az[q]);
+    }
+  }
+}
+
+template <int K, int T, int WAVES, int S, int U, class L>
+static hipError_t launch_tile(const L &lay, int n, float G, float eps2, hipStream_t stream) {
+  constexpr int GW = WAVES / S;
+  const int per_block = GW * kWave * K;
+  const int blocks = (n + per_block - 1) / per_block;
+  const int n_tiles = (n + T - 1) / T;
+  const int tiles_per_part = (n_tiles + S - 1) / S;
+  hipLaunchKernelGGL((force_tile_kernel<K, T, WAVES, S, U, L>), dim3(blocks),
+                     dim3(WAVES * kWave), 0, stream, lay, n, n_tiles, tiles_per_part, G, eps2);
+  return hipGetLastError();
+}
+
+// (id, K, T, waves, S, unroll).  Ids are part of the ABI (nbody_accel_variant).
+#define NBODY_FORCE_VARIANTS(X) \
+  X(0, 1, 256, 4, 1, 4)         \
+  X(1, 2, 256, 4, 1, 4)         \
+  X(2, 4, 256, 4, 1, 4)         \
+  X(3, 8, 256, 4, 1, 2)         \
+  X(4, 4, 512, 4, 1, 4)         \
+  X(5, 8, 512, 4, 1, 2)         \
+  X(6, 4, 256, 4, 1, 1)         \
+  X(7, 4, 256, 4, 1, 8)         \
+  X(8, 1, 256, 8, 2, 4)         \
+  X(9, 2, 256, 8, 2, 4)         \
+  X(10, 1, 256, 16, 4, 4)       \
+  X(11, 1, 64, 16, 16, 4)       \
+  X(12, 2, 128, 16, 8, 4)       \
+  X(13, 4, 256, 8, 2, 4)
+
+static const ForceVariant kVariants[] = {
+#define X(id, K, T, W, S, U) {K, T, W, S, U},
+    NBODY_FORCE_VARIANTS(X)
+#undef X
+};
+
+int force_variant_count() { return (int)(sizeof(kVariants) / sizeof(kVariants[0])); }
+
+const ForceVariant *force_variant(int v) {
+  return (v >= 0 && v < force_variant_count()) ? &kVariants[v] : nullptr;
+}
+
+// Chooses a variant that gives the chip (256 CUs x 4 SIMDs) at least ~2
+// wavefronts per SIMD where n allows, with the most i-bodies per lane that
+// still does so.
+int force_variant_for_n(int64_t n) {
+  if (n <= 32768) return 11;   // 64 i per block, j split 16 ways
+  if (n <= 131072) return 12;  // 128 i per block, j split 8 ways
+  if (n <= 262144) return 9;   // 512 i per block, j split 2 ways
+  if (n <= 524288) return 1;   // 512 i per block
+  return 2;                    // 1024 i per block
+}
+
+template <class L>
+static hipError_t dispatch(int v, const L &lay, int n, float G, float eps2, hipStream_t stream) {
+  switch (v) {
+#define X(id, K, T, W, S, U) \
+  case id:                   \
+    return launch_tile<K, T, W, S, U>(lay, n, G, eps2, stream);
+    NBODY_FORCE_VARIANTS(X)
+#undef X
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_force(int variant, Layout layout, const BodyArrays &b, int n, float G,
+                        float eps2, hipStream_t stream) {
+  switch (layout) {
+    case Layout::Aos4: {
+      LayoutAos4 lay{reinterpret_cast<const float4 *>(b.posmass),
+                     reinterpret_cast<float4 *>(b.accel4)};
+      return dispatch(variant, lay, n, G, eps2, stream);
+    }
+    case Layout::Aos3: {
+      LayoutAos3 lay{b.pos3, b.mass, b.accel3};
+      return dispatch(variant, lay, n, G, eps2, stream);
+    }
+    case Layout::Soa: {
+      LayoutSoa lay{b.x, b.y, b.z, b.m, b.ax, b.ay, b.az};
+      return dispatch(variant, lay, n, G, eps2, stream);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace nbody

@@ -1,0 +1,95 @@
+// Shared device helpers of libnbody (gfx950).  Internal header: not part of
+// the C ABI.
+//
+// Arithmetic contract.  Every fused multiply-add is written out with
+// __builtin_fmaf and the library is compiled with -ffp-contract=off, so the
+// sequence of roundings is fixed by the source and identical in every kernel
+// that uses these helpers; that is what makes the float4, float3 and SoA
+// paths bitwise equal to one another.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nbody {
+
+constexpr int kWave = 64;  // CDNA wavefront width
+
+// One body-body term of the softened sum (README "CUDA N-Body Simulation",
+// section 1.2; the 20-flop pair step of "Cuda Nbody Notes"):
+//   r = x_j - x_i,  d2 = |r|^2 + eps^2,  inv = d2^{-1/2} (v_rsq_f32),
+//   s = m_j inv^3,  p += s r.
+// For j = i, r = 0 and the term is exactly zero (eps^2 > 0).  A padding body
+// of mass 0 gives s = 0 and leaves p unchanged.
+__device__ __forceinline__ void pair_accel(float xj, float yj, float zj, float mj,
+                                           float xi, float yi, float zi, float eps2,
+                                           float &px, float &py, float &pz) {
+  const float dx = xj - xi;
+  const float dy = yj - yi;
+  const float dz = zj - zi;
+  float d2 = __builtin_fmaf(dx, dx, eps2);
+  d2 = __builtin_fmaf(dy, dy, d2);
+  d2 = __builtin_fmaf(dz, dz, d2);
+  const float inv = __builtin_amdgcn_rsqf(d2);
+  const float s = (mj * inv) * (inv * inv);
+  px = __builtin_fmaf(s, dx, px);
+  py = __builtin_fmaf(s, dy, py);
+  pz = __builtin_fmaf(s, dz, pz);
+}
+
+// (|r|^2 + eps^2)^{-1/2} for one pair: the potential term of the energy is
+// m_j times this, with the j = i term dropped by the caller's index test.
+__device__ __forceinline__ float pair_rsq(float xj, float yj, float zj, float xi, float yi,
+                                          float zi, float eps2) {
+  const float dx = xj - xi;
+  const float dy = yj - yi;
+  const float dz = zj - zi;
+  float d2 = __builtin_fmaf(dx, dx, eps2);
+  d2 = __builtin_fmaf(dy, dy, d2);
+  d2 = __builtin_fmaf(dz, dz, d2);
+  return __builtin_amdgcn_rsqf(d2);
+}
+
+// ---------------------------------------------------------------------------
+// Body loaders / storers for the three layouts.  load(j) returns (x, y, z, m);
+// the caller clamps j into [0, n) and zeroes m for padding.
+// ---------------------------------------------------------------------------
+struct LayoutAos4 {
+  const float4 *pm;
+  float4 *out;
+  __device__ __forceinline__ float4 load(int j) const { return pm[j]; }
+  __device__ __forceinline__ void store(int i, float ax, float ay, float az) const {
+    out[i] = make_float4(ax, ay, az, 0.0f);
+  }
+};
+
+struct LayoutAos3 {
+  const float *pos;   // [n][3]
+  const float *mass;  // [n]
+  float *out;         // [n][3]
+  __device__ __forceinline__ float4 load(int j) const {
+    const size_t b = (size_t)j * 3;
+    return make_float4(pos[b], pos[b + 1], pos[b + 2], mass[j]);
+  }
+  __device__ __forceinline__ void store(int i, float ax, float ay, float az) const {
+    const size_t b = (size_t)i * 3;
+    out[b] = ax;
+    out[b + 1] = ay;
+    out[b + 2] = az;
+  }
+};
+
+struct LayoutSoa {
+  const float *x, *y, *z, *m;
+  float *ax, *ay, *az;
+  __device__ __forceinline__ float4 load(int j) const {
+    return make_float4(x[j], y[j], z[j], m[j]);
+  }
+  __device__ __forceinline__ void store(int i, float vx, float vy, float vz) const {
+    ax[i] = vx;
+    ay[i] = vy;
+    az[i] = vz;
+  }
+};
+
+}  // namespace nbody

@@ -1,0 +1,61 @@
+// Host-side launchers of libnbody, shared between the kernel translation
+// units and the C ABI layer.  Internal header: not part of the C ABI.
+//
+// Every launcher assumes its arguments were validated by the C ABI layer
+// (n >= 1, pointers non-null, aligned and disjoint as documented in nbody.h)
+// and returns the hipError_t of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nbody {
+
+// Force-pass tiling of one compiled variant.
+struct ForceVariant {
+  int bodies_per_lane;  // K: i-bodies held in registers by each lane
+  int tile;             // T: j-bodies per LDS tile (two-level summation chunk)
+  int waves;            // waves per block
+  int split;            // S: j-parts per block (waves / S waves per part)
+  int unroll;           // unroll of the inner j loop
+};
+
+int force_variant_count();
+const ForceVariant *force_variant(int v);
+int force_variant_for_n(int64_t n);
+
+enum class Layout { Aos4, Aos3, Soa };
+
+struct BodyArrays {
+  // Aos4
+  const float *posmass = nullptr;
+  float *accel4 = nullptr;
+  // Aos3
+  const float *pos3 = nullptr;
+  const float *mass = nullptr;
+  float *accel3 = nullptr;
+  // Soa
+  const float *x = nullptr, *y = nullptr, *z = nullptr, *m = nullptr;
+  float *ax = nullptr, *ay = nullptr, *az = nullptr;
+};
+
+hipError_t launch_force(int variant, Layout layout, const BodyArrays &b, int n, float G,
+                        float eps2, hipStream_t stream);
+
+// Two-pass decomposition over j chunks.
+size_t splitj_workspace_bytes(int64_t n, int64_t j_chunk);
+hipError_t launch_splitj(const float *posmass, int n, float G, float eps2, float *accel,
+                         int j_chunk, void *workspace, hipStream_t stream);
+
+// Integrator.
+hipError_t launch_leapfrog(float *posmass, float *vel, const float *accel, float dt, int n,
+                           hipStream_t stream);
+hipError_t launch_kick(float *vel, const float *accel, float h, int n, hipStream_t stream);
+
+// Energy.
+size_t energy_workspace_bytes(int64_t n);
+hipError_t launch_energy(const float *posmass, const float *vel, int n, float G, float eps2,
+                         void *workspace, double *stats, hipStream_t stream);
+
+}  // namespace nbody

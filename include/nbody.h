@@ -1,0 +1,183 @@
+/*
+ * nbody.h -- C ABI of libnbody.so: direct all-pairs softened gravity on one
+ * AMD Instinct MI355X (gfx950), with a kick-drift-kick leapfrog integrator
+ * and a deterministic energy / momentum reduction.
+ *
+ * The operation (restated from the sources, cited by page and section):
+ *   a_i = G * sum_j m_j r_ij / (|r_ij|^2 + eps^2)^{3/2},  r_ij = x_j - x_i,
+ * the softened all-pairs acceleration of the "CUDA N-Body Simulation"
+ * README (LienoPC/N-BodySimulation), section 1.2, evaluated over float4
+ * (x, y, z, m) bodies as in that README's section 2.2 and the tiled kernel of
+ * "Cuda Nbody Notes".  The j = i term is included branch-free: r_ii = 0 makes
+ * it exactly zero when eps^2 > 0 (README section 1.2, closing remark), which
+ * is why eps2 must be > 0.  The host hands positions and masses over and gets
+ * accelerations back, the GRAPE-style data flow of the "CAL programming (4)"
+ * page (section "N-body computation").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every array pointer is a DEVICE pointer to memory the caller owns (for
+ *    instance a torch tensor's data_ptr()).  The library never allocates,
+ *    frees, copies to the host or synchronises; every call only enqueues
+ *    kernels on `stream` (a hipStream_t passed as void*; NULL = the null
+ *    stream) and returns.  Results are ready when the stream reaches them.
+ *  - float4 arrays are float[n][4], 16-byte aligned; float3 arrays are
+ *    float[n][3] and plain float arrays float[n], 4-byte aligned.
+ *  - n is the body count: 0 <= n <= NBODY_MAX_N.  n == 0 is a no-op that
+ *    returns NBODY_OK and touches no pointer.
+ *  - Arguments are validated before anything is enqueued; on any error
+ *    nothing is enqueued.  A failed launch returns NBODY_ERR_HIP.
+ *  - NaN or Inf inside the arrays are not checked; they propagate.
+ *  - Outputs are in input order: row i of an output belongs to body i.
+ *  - Results are bitwise reproducible for a given (n, entry point, variant):
+ *    every sum has a fixed order and no atomics are used.  See
+ *    NBODY_SUMMATION_ORDER below.
+ *  - The library keeps no state; calls on different streams may overlap as
+ *    long as they do not write memory another call reads.
+ */
+#ifndef NBODY_H
+#define NBODY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NBODY_ABI_VERSION 1
+
+/* Largest accepted body count (2^30).  Body indices are 32-bit inside the
+ * kernels; byte offsets are 64-bit. */
+#define NBODY_MAX_N ((int64_t)1 << 30)
+
+typedef enum nbody_status {
+    NBODY_OK = 0,
+    NBODY_ERR_INVALID_ARG = -1, /* null pointer with n > 0, n out of range,
+                                   eps2 <= 0 or not finite, G / dt not finite,
+                                   unknown variant, bad split size */
+    NBODY_ERR_ALIGNMENT = -2,   /* a float4 array not 16-byte aligned, or a
+                                   float array not 4-byte aligned */
+    NBODY_ERR_ALIAS = -3,       /* an output overlaps an array it must not */
+    NBODY_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than required */
+    NBODY_ERR_HIP = -5          /* a HIP launch or runtime call failed */
+} nbody_status;
+
+/* Static, NUL-terminated description of a status code.  Never NULL. */
+const char *nbody_status_string(int status);
+
+/* NBODY_ABI_VERSION of the built library. */
+int nbody_abi_version(void);
+
+/* ---------------------------------------------------------------------------
+ * NBODY_SUMMATION_ORDER (documentation only).
+ * For body i, the j range [0, n) is padded to a multiple of the variant's
+ * tile width T with bodies of mass 0 (their contribution is exactly +0).  j
+ * runs in tiles; inside a tile the three components are accumulated from
+ * zero in ascending j with one fused multiply-add per component, and the
+ * tile's partial sum is then added to the running sum (two-level summation,
+ * which keeps fp32 rounding at ~u*sqrt(n/T) instead of ~u*sqrt(n)).  A
+ * variant that splits j over S parts gives each part a contiguous range of
+ * tiles and adds the S part sums in ascending part order.  Finally the sum
+ * is multiplied by G.
+ * ------------------------------------------------------------------------- */
+
+/* Accelerations of all n bodies.
+ *   posmass    [n] float4 (x, y, z, m), read only.
+ *   G          gravitational constant (finite).
+ *   eps2       squared softening length eps^2 (> 0, finite).  The README's
+ *              constants table calls this EPS2 (section 6.1).
+ *   accel_out  [n] float4, written: (ax, ay, az, 0).  Must not overlap
+ *              posmass (NBODY_ERR_ALIAS).
+ * The library picks a variant from n (nbody_accel_variant_for_n). */
+int nbody_accel(const float *posmass, int64_t n, float G, float eps2,
+                float *accel_out, void *stream);
+
+/* The same pass with an explicit compiled variant (0 <= variant <
+ * nbody_accel_variant_count()).  For tuning sweeps and tests. */
+int nbody_accel_variant(const float *posmass, int64_t n, float G, float eps2,
+                        float *accel_out, int variant, void *stream);
+
+/* Number of compiled force variants. */
+int nbody_accel_variant_count(void);
+
+/* Describes variant v: bodies per lane, tile width T, waves per block, j
+ * split S.  Returns NBODY_ERR_INVALID_ARG for an unknown v; any pointer
+ * may be NULL to skip that field. */
+int nbody_accel_variant_info(int v, int *bodies_per_lane, int *tile,
+                             int *waves_per_block, int *split);
+
+/* The variant nbody_accel uses for n bodies. */
+int nbody_accel_variant_for_n(int64_t n);
+
+/* Two-pass ("2D") decomposition: the j range is cut into chunks of j_chunk
+ * bodies (j_chunk a multiple of 32, >= 32); a first kernel writes one
+ * float4 partial per (chunk, body) into the workspace, a second adds the
+ * chunks of each body in ascending chunk order and multiplies by G.  This
+ * is the N x N grid with per-block partial sums and an atomic-free second
+ * pass of the README's sections 3.2-3.3, with the chunk as the tunable.
+ *   workspace  device memory of at least
+ *              nbody_accel_splitj_workspace_bytes(n, j_chunk) bytes, 16-byte
+ *              aligned; must not overlap posmass or accel_out.  Contents on
+ *              return are unspecified.
+ * Other arguments as nbody_accel. */
+int nbody_accel_splitj(const float *posmass, int64_t n, float G, float eps2,
+                       float *accel_out, int64_t j_chunk, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/* Workspace bytes nbody_accel_splitj needs (0 for n == 0; 0 for an invalid
+ * j_chunk). */
+size_t nbody_accel_splitj_workspace_bytes(int64_t n, int64_t j_chunk);
+
+/* The force pass on other body layouts; same arithmetic and order as
+ * nbody_accel for the same n, so the outputs are bitwise equal to its
+ * (ax, ay, az).  README section 3.5 compares float4 against 12-byte float3
+ * records.
+ *   nbody_accel_f3aos: pos [n] float3 (x, y, z), mass [n] float,
+ *                      accel_out [n] float3 (ax, ay, az).
+ *   nbody_accel_soa:   x, y, z, m, ax, ay, az: [n] float each.
+ * No output may overlap an input. */
+int nbody_accel_f3aos(const float *pos, const float *mass, int64_t n, float G,
+                      float eps2, float *accel_out, void *stream);
+int nbody_accel_soa(const float *x, const float *y, const float *z,
+                    const float *m, int64_t n, float G, float eps2, float *ax,
+                    float *ay, float *az, void *stream);
+
+/* Kick and drift of the leapfrog scheme, README section 1.3:
+ *   v <- v + (dt/2) a ;  x <- x + dt v   (per body, in place)
+ *   posmass  [n] float4, xyz updated, m (w) left bit-for-bit unchanged.
+ *   vel      [n] float4, xyz updated, w left unchanged.
+ *   accel    [n] float4, a(x) at the current positions (w ignored).
+ * The three arrays must be pairwise disjoint.  A full kick-drift-kick step
+ * is nbody_leapfrog_step, nbody_accel at the new positions, then
+ * nbody_kick(vel, accel, dt/2). */
+int nbody_leapfrog_step(float *posmass, float *vel, const float *accel,
+                        float dt, int64_t n, void *stream);
+
+/* Closing half-kick v <- v + h a (h = dt/2 for kick-drift-kick).
+ *   vel [n] float4 in place (w unchanged); accel [n] float4, disjoint. */
+int nbody_kick(float *vel, const float *accel, float h, int64_t n,
+               void *stream);
+
+/* Energy and momentum.  stats_out (device, 8 doubles) receives
+ *   {K, W, K + W, Px, Py, Pz, M, 0}
+ * with K = sum m |v|^2 / 2, P = sum m v, M = sum m and
+ * W = -G sum_{i<j} m_i m_j / sqrt(|x_i - x_j|^2 + eps^2), the softened
+ * potential whose negative gradient is the acceleration above (the pages
+ * print no energy; this is the plain reading).  Pair terms are fp32 (the
+ * j = i term is excluded by an index test); per-body sums go to fp64 per
+ * tile and every cross-body sum is fp64 in a fixed tree order.
+ *   workspace  >= nbody_energy_workspace_bytes(n) bytes, 16-byte aligned,
+ *              disjoint from every other argument.
+ *   stats_out  8 doubles, 8-byte aligned. */
+int nbody_energy(const float *posmass, const float *vel, int64_t n, float G,
+                 float eps2, void *workspace, size_t workspace_bytes,
+                 double *stats_out, void *stream);
+
+size_t nbody_energy_workspace_bytes(int64_t n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NBODY_H */

@@ -1,0 +1,170 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function the
+header declares, and its pure host logic (status strings, variant table,
+workspace sizes, argument validation) behaves as documented.  Nothing here
+launches a kernel: every call below is rejected by validation, or is n == 0,
+before the library would touch the HIP runtime."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import direct_all_pairs_softened_amd as nb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nbody.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nbody_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return nb.load_library()
+
+
+def test_header_and_binding_agree():
+    assert sorted(nb.EXPORTS) == _declared_functions()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.nbody_abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5):
+        s = nb.status_string(code)
+        assert s and s != "unknown status"
+    assert nb.status_string(42) == "unknown status"
+
+
+def test_variant_table(lib):
+    count = nb.nbody_accel_variant_count()
+    assert count >= 8
+    for v in range(count):
+        info = nb.nbody_accel_variant_info(v)
+        assert info["bodies_per_lane"] in (1, 2, 4, 8)
+        assert info["waves_per_block"] % info["split"] == 0
+        assert (info["split"] * info["tile"]) % (64 * info["waves_per_block"]) == 0
+    with pytest.raises(nb.NBodyError):
+        nb.nbody_accel_variant_info(count)
+    for n in (1, 1000, 1024, 16384, 131072, 1 << 20, 1000003, nb.NBODY_MAX_N):
+        assert 0 <= nb.nbody_accel_variant_for_n(n) < count
+
+
+def test_workspace_sizes(lib):
+    assert nb.nbody_accel_splitj_workspace_bytes(0, 32) == 0
+    assert nb.nbody_accel_splitj_workspace_bytes(100, 31) == 0      # not a multiple of 32
+    assert nb.nbody_accel_splitj_workspace_bytes(100, 16) == 0      # below 32
+    assert nb.nbody_accel_splitj_workspace_bytes(131072, 32) == 4096 * 131072 * 16
+    assert nb.nbody_accel_splitj_workspace_bytes(1000, 256) == 4 * 1000 * 16
+    assert nb.nbody_energy_workspace_bytes(0) == 0
+    assert nb.nbody_energy_workspace_bytes(-1) == 0
+    assert nb.nbody_energy_workspace_bytes(1) >= 64
+    assert nb.nbody_energy_workspace_bytes(1 << 20) >= 64 * ((1 << 20) // 256)
+
+
+# Fake device addresses: validation rejects these calls before anything is
+# enqueued or dereferenced.
+A = 0x10000000
+B = 0x20000000
+C = 0x30000000
+D = 0x40000000
+vp = ctypes.c_void_p
+
+
+def test_accel_validation(lib):
+    f = lib.nbody_accel
+    assert f(vp(A), 0, 1.0, 1e-4, vp(B), None) == nb.NBODY_OK              # n == 0: no-op
+    assert f(None, 0, 1.0, 1e-4, None, None) == nb.NBODY_OK
+    assert f(None, 10, 1.0, 1e-4, vp(B), None) == nb.NBODY_ERR_INVALID_ARG
+    assert f(vp(A), 10, 1.0, 1e-4, None, None) == nb.NBODY_ERR_INVALID_ARG
+    assert f(vp(A), -1, 1.0, 1e-4, vp(B), None) == nb.NBODY_ERR_INVALID_ARG
+    assert f(vp(A), nb.NBODY_MAX_N + 1, 1.0, 1e-4, vp(B), None) == nb.NBODY_ERR_INVALID_ARG
+    assert f(vp(A), 10, 1.0, 0.0, vp(B), None) == nb.NBODY_ERR_INVALID_ARG   # eps2 == 0
+    assert f(vp(A), 10, 1.0, -1e-4, vp(B), None) == nb.NBODY_ERR_INVALID_ARG
+    assert f(vp(A), 10, 1.0, float("nan"), vp(B), None) == nb.NBODY_ERR_INVALID_ARG
+    assert f(vp(A), 10, float("inf"), 1e-4, vp(B), None) == nb.NBODY_ERR_INVALID_ARG
+    assert f(vp(A + 4), 10, 1.0, 1e-4, vp(B), None) == nb.NBODY_ERR_ALIGNMENT
+    assert f(vp(A), 10, 1.0, 1e-4, vp(B + 8), None) == nb.NBODY_ERR_ALIGNMENT
+    assert f(vp(A), 10, 1.0, 1e-4, vp(A), None) == nb.NBODY_ERR_ALIAS
+    assert f(vp(A), 10, 1.0, 1e-4, vp(A + 16 * 9), None) == nb.NBODY_ERR_ALIAS
+    g = lib.nbody_accel_variant
+    assert g(vp(A), 10, 1.0, 1e-4, vp(B), -1, None) == nb.NBODY_ERR_INVALID_ARG
+    assert g(vp(A), 10, 1.0, 1e-4, vp(B), 10 ** 6, None) == nb.NBODY_ERR_INVALID_ARG
+
+
+def test_layout_variants_validation(lib):
+    f3 = lib.nbody_accel_f3aos
+    assert f3(vp(A), vp(B), 0, 1.0, 1e-4, vp(C), None) == nb.NBODY_OK
+    assert f3(vp(A), None, 10, 1.0, 1e-4, vp(C), None) == nb.NBODY_ERR_INVALID_ARG
+    assert f3(vp(A + 2), vp(B), 10, 1.0, 1e-4, vp(C), None) == nb.NBODY_ERR_ALIGNMENT
+    assert f3(vp(A), vp(B), 10, 1.0, 1e-4, vp(A + 12), None) == nb.NBODY_ERR_ALIAS
+    assert f3(vp(A), vp(B), 10, 1.0, 1e-4, vp(B - 8), None) == nb.NBODY_ERR_ALIAS
+    soa = lib.nbody_accel_soa
+    ptrs = [vp(A + k * 0x1000) for k in range(7)]
+    assert soa(*ptrs[:4], 0, 1.0, 1e-4, *ptrs[4:], None) == nb.NBODY_OK
+    bad = list(ptrs)
+    bad[5] = None
+    assert soa(*bad[:4], 10, 1.0, 1e-4, *bad[4:], None) == nb.NBODY_ERR_INVALID_ARG
+    bad = list(ptrs)
+    bad[6] = ptrs[0]
+    assert soa(*bad[:4], 10, 1.0, 1e-4, *bad[4:], None) == nb.NBODY_ERR_ALIAS
+    bad = list(ptrs)
+    bad[5] = ptrs[4]
+    assert soa(*bad[:4], 10, 1.0, 1e-4, *bad[4:], None) == nb.NBODY_ERR_ALIAS
+    bad = list(ptrs)
+    bad[2] = vp(A + 0x2001)
+    assert soa(*bad[:4], 10, 1.0, 1e-4, *bad[4:], None) == nb.NBODY_ERR_ALIGNMENT
+
+
+def test_splitj_validation(lib):
+    f = lib.nbody_accel_splitj
+    need = nb.nbody_accel_splitj_workspace_bytes(1000, 256)
+    assert f(vp(A), 1000, 1.0, 1e-4, vp(B), 48, vp(C), need, None) == nb.NBODY_ERR_INVALID_ARG
+    assert f(vp(A), 1000, 1.0, 1e-4, vp(B), 16, vp(C), need, None) == nb.NBODY_ERR_INVALID_ARG
+    assert f(vp(A), 1000, 1.0, 1e-4, vp(B), 256, None, need, None) == nb.NBODY_ERR_WORKSPACE
+    assert f(vp(A), 1000, 1.0, 1e-4, vp(B), 256, vp(C), need - 1, None) == nb.NBODY_ERR_WORKSPACE
+    assert f(vp(A), 1000, 1.0, 1e-4, vp(B), 256, vp(C + 8), need, None) == nb.NBODY_ERR_ALIGNMENT
+    assert f(vp(A), 1000, 1.0, 1e-4, vp(B), 256, vp(A), need, None) == nb.NBODY_ERR_ALIAS
+    # more than 65535 chunks
+    assert f(vp(A), 32 * 70000, 1.0, 1e-4, vp(B), 32, vp(C), 1 << 62, None) == nb.NBODY_ERR_INVALID_ARG
+    assert f(vp(A), 0, 1.0, 1e-4, vp(B), 32, None, 0, None) == nb.NBODY_OK
+
+
+def test_integrator_validation(lib):
+    lf = lib.nbody_leapfrog_step
+    assert lf(vp(A), vp(B), vp(C), 1e-3, 0, None) == nb.NBODY_OK
+    assert lf(vp(A), vp(B), vp(C), float("nan"), 10, None) == nb.NBODY_ERR_INVALID_ARG
+    assert lf(vp(A), None, vp(C), 1e-3, 10, None) == nb.NBODY_ERR_INVALID_ARG
+    assert lf(vp(A), vp(B + 4), vp(C), 1e-3, 10, None) == nb.NBODY_ERR_ALIGNMENT
+    assert lf(vp(A), vp(A + 16), vp(C), 1e-3, 10, None) == nb.NBODY_ERR_ALIAS
+    assert lf(vp(A), vp(B), vp(B), 1e-3, 10, None) == nb.NBODY_ERR_ALIAS
+    k = lib.nbody_kick
+    assert k(vp(A), vp(B), 5e-4, 0, None) == nb.NBODY_OK
+    assert k(vp(A), vp(A), 5e-4, 10, None) == nb.NBODY_ERR_ALIAS
+    assert k(vp(A), vp(B), float("inf"), 10, None) == nb.NBODY_ERR_INVALID_ARG
+
+
+def test_energy_validation(lib):
+    e = lib.nbody_energy
+    need = nb.nbody_energy_workspace_bytes(1000)
+    assert e(vp(A), vp(B), 0, 1.0, 1e-4, None, 0, None, None) == nb.NBODY_OK
+    assert e(vp(A), vp(B), 1000, 1.0, 1e-4, vp(C), need, None, None) == nb.NBODY_ERR_INVALID_ARG
+    assert e(vp(A), vp(B), 1000, 1.0, 1e-4, vp(C), need - 8, vp(D), None) == nb.NBODY_ERR_WORKSPACE
+    assert e(vp(A), vp(B), 1000, 1.0, 1e-4, vp(C), need, vp(D + 4), None) == nb.NBODY_ERR_ALIGNMENT
+    assert e(vp(A), vp(B), 1000, 1.0, 0.0, vp(C), need, vp(D), None) == nb.NBODY_ERR_INVALID_ARG
+    assert e(vp(A), vp(B), 1000, 1.0, 1e-4, vp(A), need, vp(D), None) == nb.NBODY_ERR_ALIAS
+    assert e(vp(A), vp(B), 1000, 1.0, 1e-4, vp(C), need, vp(B + 64), None) == nb.NBODY_ERR_ALIAS
+
+
+def test_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    pm = torch.zeros(4, 4)
+    with pytest.raises(ValueError):
+        nb.nbody_accel(pm, 1.0, 1e-4, torch.zeros(4, 4))

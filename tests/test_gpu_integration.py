@@ -1,0 +1,180 @@
+"""Integrator and energy on the GPU: the kick/drift kernels against the
+oracle's kick/drift on identical inputs, the energy reduction against the
+oracle's energy, and whole kick-drift-kick runs of the project's workloads
+(energy drift, momentum, accelerations at the final step checked by the
+oracle on the GPU's own state, time reversibility)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import direct_all_pairs_softened_amd as nb
+import oracle
+import workloads
+from parity import assert_parity, log, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+F32 = np.float32
+ULP = 2.0 ** -23
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def test_leapfrog_kernel_matches_oracle_kick_drift():
+    g = np.random.default_rng(1)
+    n = 5000
+    pm = g.uniform(-2, 2, (n, 4)).astype(F32)
+    pm[:, 3] = g.uniform(0.1, 1.0, n).astype(F32)
+    vel = g.uniform(-1, 1, (n, 4)).astype(F32)
+    vel[:, 3] = g.uniform(-9, 9, n).astype(F32)        # w must survive untouched
+    acc = g.uniform(-3, 3, (n, 4)).astype(F32)
+    dt = F32(1e-2)
+    tp, tv, ta = to_dev(pm), to_dev(vel), to_dev(acc)
+    nb.nbody_leapfrog_step(tp, tv, ta, float(dt))
+    torch.cuda.synchronize()
+    x_gpu, v_gpu = tp.cpu().numpy(), tv.cpu().numpy()
+    v_ref = oracle.kick(vel, acc, 0.5 * float(dt))
+    x_ref = oracle.drift(pm, v_ref, float(dt))
+    # v: one rounding of the exact v + h a; x: one rounding plus dt times v's.
+    assert np.all(np.abs(v_gpu[:, :3] - v_ref) <= ULP * np.abs(v_ref))
+    bound = ULP * (np.abs(x_ref) + float(dt) * np.abs(v_ref))
+    assert np.all(np.abs(x_gpu[:, :3] - x_ref) <= bound)
+    assert np.array_equal(x_gpu[:, 3], pm[:, 3])
+    assert np.array_equal(v_gpu[:, 3], vel[:, 3])
+    assert np.array_equal(ta.cpu().numpy(), acc)
+
+
+def test_kick_kernel_matches_oracle():
+    g = np.random.default_rng(2)
+    n = 4099
+    vel = g.uniform(-1, 1, (n, 4)).astype(F32)
+    acc = g.uniform(-3, 3, (n, 4)).astype(F32)
+    h = F32(5e-4)
+    tv, ta = to_dev(vel), to_dev(acc)
+    nb.nbody_kick(tv, ta, float(h))
+    torch.cuda.synchronize()
+    v = tv.cpu().numpy()
+    v_ref = oracle.kick(vel, acc, float(h))
+    assert np.all(np.abs(v[:, :3] - v_ref) <= ULP * np.abs(v_ref))
+    assert np.array_equal(v[:, 3], vel[:, 3])
+
+
+def gpu_energy(pm_np, vel_np, G, eps2):
+    return nb.energy(to_dev(pm_np), to_dev(vel_np), G, eps2)
+
+
+def ref_energy(pm_np, vel_np, G, eps2):
+    pos, mass = oracle.split_posmass(pm_np)
+    return oracle.energy(pos, vel_np, mass, float(F32(G)), float(F32(eps2)))
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 65, 1000, 4097, 70000])
+def test_energy_matches_oracle(n):
+    pm, vel = workloads.plummer(n, seed=n) if n > 1 else (
+        np.array([[0.1, 0.2, 0.3, 2.0]], F32), np.array([[1, 2, 3, 0]], F32))
+    log(f"energy n={n}")
+    e = gpu_energy(pm, vel, 1.0, 1e-4)
+    r = ref_energy(pm, vel, 1.0, 1e-4)
+    assert abs(e["K"] - r["K"]) <= 1e-12 * abs(r["K"])
+    assert abs(e["M"] - r["M"]) <= 1e-12 * r["M"]
+    if n > 1:
+        assert abs(e["W"] - r["W"]) <= 2e-6 * abs(r["W"])
+    else:
+        assert e["W"] == 0.0
+    # summation-order rounding of P scales with sum m |v|, not with |P| ~ 0
+    mv = float((pm[:, 3].astype(np.float64) *
+                np.linalg.norm(vel[:, :3].astype(np.float64), axis=1)).sum())
+    for k in ("Px", "Py", "Pz"):
+        assert abs(e[k] - r[k]) <= 1e-13 * mv
+
+
+def test_energy_two_body_closed_form():
+    pm = np.array([[0, 0, 0, 1], [3, 4, 0, 1]], F32)
+    vel = np.array([[1, 0, 0, 0], [0, 2, 0, 0]], F32)
+    e = gpu_energy(pm, vel, 1.0, 11.0)
+    assert e["K"] == 2.5
+    assert abs(e["W"] + 1.0 / 6.0) <= 1e-7
+    assert (e["Px"], e["Py"], e["Pz"], e["M"]) == (1.0, 2.0, 0.0, 2.0)
+
+
+def test_energy_deterministic():
+    pm, vel = workloads.make("plummer16k")
+    a = gpu_energy(pm, vel, 1.0, 1e-4)
+    b = gpu_energy(pm, vel, 1.0, 1e-4)
+    assert a == b
+
+
+def run_kdk(pm_np, vel_np, G, eps2, dt, steps, check_every=None):
+    pm, vel = to_dev(pm_np), to_dev(vel_np)
+    acc = torch.empty_like(pm)
+    nb.nbody_accel(pm, G, eps2, acc)
+    energies = [nb.energy(pm, vel, G, eps2)]
+    for s in range(steps):
+        nb.kdk_step(pm, vel, acc, G, eps2, dt)
+        if check_every and (s + 1) % check_every == 0:
+            energies.append(nb.energy(pm, vel, G, eps2))
+    torch.cuda.synchronize()
+    return pm, vel, acc, energies
+
+
+def test_plummer16k_ten_steps():
+    w = workloads.WORKLOADS["plummer16k"]
+    pm0, v0 = workloads.make("plummer16k")
+    pm, vel, acc, es = run_kdk(pm0, v0, w.G, w.eps2, w.dt, w.steps, check_every=w.steps)
+    drift = abs(es[-1]["E"] - es[0]["E"]) / abs(es[0]["E"])
+    log(f"plummer16k energy drift {drift:.3e}")
+    assert drift <= 1e-4
+    # accelerations at step 10, checked by the oracle on the GPU's own state
+    pm_np = pm.cpu().numpy()
+    pos, mass = oracle.split_posmass(pm_np)
+    ref = oracle.accel(pos, mass, w.G, float(F32(w.eps2)))
+    assert_parity(acc.cpu().numpy(), ref, "plummer16k step 10")
+    assert np.array_equal(pm_np[:, 3], pm0[:, 3])
+    # trajectory against the oracle's own float64 integration
+    pos0, mass0 = oracle.split_posmass(pm0)
+    x_ref, v_ref, _ = oracle.kdk(pos0, v0, mass0, w.G, float(F32(w.eps2)), float(F32(w.dt)),
+                                 w.steps)
+    dx = np.abs(pm_np[:, :3] - x_ref).max()
+    dv = np.abs(vel.cpu().numpy()[:, :3] - v_ref).max()
+    log(f"plummer16k trajectory vs oracle: max |dx| {dx:.2e}, max |dv| {dv:.2e}")
+    assert dx <= 2e-5 and dv <= 2e-5
+
+
+def test_time_reversibility():
+    pm0, v0 = workloads.plummer(4096, seed=8)
+    G, eps2, dt = 1.0, 1e-4, 1e-3
+    pm, vel, acc, _ = run_kdk(pm0, v0, G, eps2, dt, 10)
+    vel[:, :3] = -vel[:, :3]
+    nb.nbody_accel(pm, G, eps2, acc)
+    for _ in range(10):
+        nb.kdk_step(pm, vel, acc, G, eps2, dt)
+    torch.cuda.synchronize()
+    assert np.abs(pm.cpu().numpy()[:, :3] - pm0[:, :3]).max() <= 1e-5
+    assert np.abs(-vel.cpu().numpy()[:, :3] - v0[:, :3]).max() <= 1e-4
+
+
+def test_collision1m_twenty_steps():
+    """Two Plummer spheres, N = 1000003, 20 KDK steps of dt = 1e-3:
+    momentum change <= 1e-6, relative energy drift <= 1e-3, and the final
+    accelerations of sampled bodies against the oracle."""
+    w = workloads.WORKLOADS["collision1m"]
+    pm0, v0 = workloads.make("collision1m")
+    log("collision1m: integrating")
+    pm, vel, acc, es = run_kdk(pm0, v0, w.G, w.eps2, w.dt, w.steps, check_every=w.steps)
+    e0, e1 = es[0], es[-1]
+    dp = math.sqrt(sum((e1[k] - e0[k]) ** 2 for k in ("Px", "Py", "Pz")))
+    drift = abs(e1["E"] - e0["E"]) / abs(e0["E"])
+    log(f"collision1m: |dP| {dp:.3e}, energy drift {drift:.3e}")
+    assert dp <= 1e-6
+    assert drift <= 1e-3
+    pm_np = pm.cpu().numpy()
+    rows = sample_rows(w.n, 256, seed=6)
+    pos, mass = oracle.split_posmass(pm_np)
+    ref = oracle.accel_rows(pos, mass, w.G, float(F32(w.eps2)), rows)
+    assert_parity(acc.cpu().numpy()[rows], ref, "collision1m step 20")
+    assert np.array_equal(pm_np[:, 3], pm0[:, 3])

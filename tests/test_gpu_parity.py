@@ -1,0 +1,221 @@
+"""Force-pass parity on the GPU: every compiled variant and every entry point
+against the double-precision oracle, on the project's workloads and on edge
+cases (tiny, ragged, tile-edge and degenerate inputs).  All calls go through
+the C ABI binding; the oracle sees the same float32 inputs promoted to
+float64."""
+import numpy as np
+import pytest
+import torch
+
+import direct_all_pairs_softened_amd as nb
+import oracle
+import workloads
+from parity import assert_parity, errors, log, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+F32 = np.float32
+
+
+def gpu_accel(pm_np, G=1.0, eps2=1e-4, variant=None):
+    pm = torch.from_numpy(pm_np).to(DEV)
+    out = torch.full_like(pm, float("nan"))
+    if variant is None:
+        nb.nbody_accel(pm, G, eps2, out)
+    else:
+        nb.nbody_accel_variant(pm, G, eps2, out, variant)
+    torch.cuda.synchronize()
+    res = out.cpu().numpy()
+    assert np.array_equal(pm.cpu().numpy(), pm_np), "posmass was modified"
+    return res
+
+
+def ref_accel(pm_np, G=1.0, eps2=1e-4, rows=None):
+    pos, mass = oracle.split_posmass(pm_np)
+    e = float(F32(eps2))
+    g = float(F32(G))
+    if rows is None:
+        return oracle.accel(pos, mass, g, e)
+    return oracle.accel_rows(pos, mass, g, e, rows)
+
+
+SIZES = [1, 2, 3, 63, 64, 65, 255, 256, 257, 1000, 1024, 1025, 4097]
+
+
+@pytest.mark.parametrize("n", SIZES)
+def test_every_variant_small_sizes(n):
+    pm, _ = workloads.uniform_cube(n, seed=n)
+    ref = ref_accel(pm)
+    for v in range(nb.nbody_accel_variant_count()):
+        log(f"n={n} variant={v}")
+        a = gpu_accel(pm, variant=v)
+        assert np.all(a[:, 3] == 0.0)
+        if n == 1:
+            assert np.array_equal(a, np.zeros((1, 4), F32))
+            continue
+        assert_parity(a, ref, f"n={n} v={v}")
+
+
+def test_two_body_closed_form_on_gpu():
+    pm = np.array([[0, 0, 0, 1], [1, 0, 0, 1]], dtype=F32)
+    a = gpu_accel(pm, eps2=1e-4)
+    expect = float(F32(1.0)) / (1.0 + float(F32(1e-4))) ** 1.5
+    assert abs(a[0, 0] - expect) <= 1e-6 * expect
+    assert a[0, 1] == 0 and a[0, 2] == 0
+    assert a[1, 0] == -a[0, 0]
+
+
+def test_coincident_bodies_and_octahedron_centre():
+    pm = np.array([[0.5, 0.5, 0.5, 1], [0.5, 0.5, 0.5, 2]], dtype=F32)
+    assert np.array_equal(gpu_accel(pm), np.zeros((2, 4), F32))
+    pm = np.array([[0, 0, 0, 2], [1, 0, 0, .75], [-1, 0, 0, .75], [0, 1, 0, .75],
+                   [0, -1, 0, .75], [0, 0, 1, .75], [0, 0, -1, .75]], dtype=F32)
+    a = gpu_accel(pm)
+    assert np.abs(a[0, :3]).max() <= 1e-6
+
+
+def test_uniform1k_workload():
+    w = workloads.WORKLOADS["uniform1k"]
+    pm, _ = workloads.make("uniform1k")
+    a = gpu_accel(pm, w.G, w.eps2)
+    assert_parity(a, ref_accel(pm, w.G, w.eps2), "uniform1k")
+    m = pm[:, 3].astype(np.float64)
+    ag = a[:, :3].astype(np.float64)
+    net = np.linalg.norm((m[:, None] * ag).sum(axis=0))
+    assert net / (m * np.linalg.norm(ag, axis=1)).sum() <= 1e-6
+
+
+def test_plummer16k_full_parity():
+    w = workloads.WORKLOADS["plummer16k"]
+    pm, _ = workloads.make("plummer16k")
+    ref = ref_accel(pm, w.G, w.eps2)
+    for v in (None, 0, 2, 9, 11, 12):
+        assert_parity(gpu_accel(pm, w.G, w.eps2, v), ref, f"plummer16k v={v}")
+
+
+def test_lognormal128k_sampled():
+    w = workloads.WORKLOADS["lognormal128k"]
+    pm, _ = workloads.make("lognormal128k")
+    rows = sample_rows(w.n, 1024, seed=1)
+    ref = ref_accel(pm, w.G, w.eps2, rows)
+    a = gpu_accel(pm, w.G, w.eps2)
+    assert_parity(a[rows], ref, "lognormal128k")
+
+
+def test_repeat_is_bitwise_identical():
+    pm, _ = workloads.make("plummer16k")
+    for v in (None, 2, 11):
+        assert np.array_equal(gpu_accel(pm, variant=v), gpu_accel(pm, variant=v))
+
+
+def test_power_of_two_homogeneity_bitwise():
+    pm, _ = workloads.uniform_cube(3000, seed=5)
+    a = gpu_accel(pm)
+    assert np.array_equal(gpu_accel(pm, G=2.0), 2 * a)
+    pm2 = pm.copy()
+    pm2[:, 3] *= 2
+    assert np.array_equal(gpu_accel(pm2), 2 * a)
+
+
+@pytest.mark.parametrize("variant", [2, 11])
+def test_ragged_equals_explicit_zero_mass_padding(variant):
+    """n = 1000 against the same bodies padded to 1024 with explicit
+    zero-mass bodies elsewhere: the padding slots add exactly +0."""
+    info = nb.nbody_accel_variant_info(variant)
+    n, npad = 1000, 1024
+    assert -(-n // info["tile"]) == -(-npad // info["tile"])  # same tile count
+    pm, _ = workloads.uniform_cube(n, seed=9)
+    pad = np.zeros((npad, 4), F32)
+    pad[:n] = pm
+    pad[n:, :3] = np.random.default_rng(0).uniform(-3, 3, (npad - n, 3)).astype(F32)
+    a = gpu_accel(pm, variant=variant)
+    b = gpu_accel(pad, variant=variant)
+    assert np.array_equal(a, b[:n])
+
+
+def test_layouts_bitwise_equal():
+    for name in ("uniform1k", "plummer16k"):
+        w = workloads.WORKLOADS[name]
+        pm, _ = workloads.make(name)
+        a4 = gpu_accel(pm, w.G, w.eps2)
+        t = torch.from_numpy(pm).to(DEV)
+        pos3 = t[:, :3].contiguous()
+        mass = t[:, 3].contiguous()
+        a3 = torch.full((w.n, 3), float("nan"), device=DEV)
+        nb.nbody_accel_f3aos(pos3, mass, w.G, w.eps2, a3)
+        cols = [t[:, k].contiguous() for k in range(4)]
+        outs = [torch.full((w.n,), float("nan"), device=DEV) for _ in range(3)]
+        nb.nbody_accel_soa(*cols, w.G, w.eps2, *outs)
+        torch.cuda.synchronize()
+        assert np.array_equal(a3.cpu().numpy(), a4[:, :3]), name
+        soa = np.stack([o.cpu().numpy() for o in outs], axis=1)
+        assert np.array_equal(soa, a4[:, :3]), name
+
+
+@pytest.mark.parametrize("j_chunk", [32, 64, 256, 1024, 4096])
+def test_splitj_parity(j_chunk):
+    for n in (1, 65, 1000, 4097):
+        pm, _ = workloads.uniform_cube(n, seed=3)
+        t = torch.from_numpy(pm).to(DEV)
+        out = torch.full_like(t, float("nan"))
+        ws = torch.empty(max(nb.nbody_accel_splitj_workspace_bytes(n, j_chunk), 16),
+                         dtype=torch.uint8, device=DEV)
+        log(f"splitj n={n} J={j_chunk}")
+        nb.nbody_accel_splitj(t, 1.0, 1e-4, out, j_chunk, ws)
+        torch.cuda.synchronize()
+        a = out.cpu().numpy()
+        assert np.all(a[:, 3] == 0)
+        if n == 1:
+            assert np.array_equal(a, np.zeros((1, 4), F32))
+        else:
+            assert_parity(a, ref_accel(pm), f"splitj n={n} J={j_chunk}")
+
+
+def test_splitj_lognormal128k_sampled_and_deterministic():
+    w = workloads.WORKLOADS["lognormal128k"]
+    pm, _ = workloads.make("lognormal128k")
+    rows = sample_rows(w.n, 512, seed=2)
+    ref = ref_accel(pm, w.G, w.eps2, rows)
+    t = torch.from_numpy(pm).to(DEV)
+    for j_chunk in (256, 4096):
+        ws = torch.empty(nb.nbody_accel_splitj_workspace_bytes(w.n, j_chunk),
+                         dtype=torch.uint8, device=DEV)
+        outs = []
+        for _ in range(2):
+            out = torch.empty_like(t)
+            nb.nbody_accel_splitj(t, w.G, w.eps2, out, j_chunk, ws)
+            torch.cuda.synchronize()
+            outs.append(out.cpu().numpy())
+        assert np.array_equal(outs[0], outs[1])
+        assert_parity(outs[0][rows], ref, f"splitj lognormal128k J={j_chunk}")
+
+
+def test_plummer1m_sampled_all_layouts():
+    w = workloads.WORKLOADS["plummer1m"]
+    pm, _ = workloads.make("plummer1m")
+    rows = sample_rows(w.n, 384, seed=4)
+    log("plummer1m: oracle rows")
+    ref = ref_accel(pm, w.G, w.eps2, rows)
+    a4 = gpu_accel(pm, w.G, w.eps2)
+    assert_parity(a4[rows], ref, "plummer1m float4")
+    t = torch.from_numpy(pm).to(DEV)
+    a3 = torch.empty((w.n, 3), device=DEV)
+    nb.nbody_accel_f3aos(t[:, :3].contiguous(), t[:, 3].contiguous(), w.G, w.eps2, a3)
+    cols = [t[:, k].contiguous() for k in range(4)]
+    outs = [torch.empty((w.n,), device=DEV) for _ in range(3)]
+    nb.nbody_accel_soa(*cols, w.G, w.eps2, *outs)
+    torch.cuda.synchronize()
+    assert np.array_equal(a3.cpu().numpy(), a4[:, :3])
+    assert np.array_equal(np.stack([o.cpu().numpy() for o in outs], axis=1), a4[:, :3])
+
+
+def test_collision1m_ragged_sampled():
+    w = workloads.WORKLOADS["collision1m"]
+    pm, _ = workloads.make("collision1m")
+    rows = sample_rows(w.n, 384, seed=5)
+    log("collision1m: oracle rows")
+    ref = ref_accel(pm, w.G, w.eps2, rows)
+    a = gpu_accel(pm, w.G, w.eps2)
+    assert np.all(a[:, 3] == 0)
+    assert_parity(a[rows], ref, "collision1m")
