@@ -139,10 +139,14 @@ def test_plummer16k_ten_steps():
     pos0, mass0 = oracle.split_posmass(pm0)
     x_ref, v_ref, _ = oracle.kdk(pos0, v0, mass0, w.G, float(F32(w.eps2)), float(F32(w.dt)),
                                  w.steps)
-    dx = np.abs(pm_np[:, :3] - x_ref).max()
-    dv = np.abs(vel.cpu().numpy()[:, :3] - v_ref).max()
-    log(f"plummer16k trajectory vs oracle: max |dx| {dx:.2e}, max |dv| {dv:.2e}")
-    assert dx <= 2e-5 and dv <= 2e-5
+    # ten fp32 drifts round x ten times (~0.5 ulp each), so the bound scales
+    # with |x|: untruncated Plummer bodies reach |x| ~ 10^2 where 1 ulp ~ 1e-5
+    dx = np.abs(pm_np[:, :3] - x_ref)
+    dv = np.abs(vel.cpu().numpy()[:, :3] - v_ref)
+    log(f"plummer16k trajectory vs oracle: max |dx| {dx.max():.2e}, "
+        f"max |dx|/(|x|+1) {(dx / (np.abs(x_ref) + 1)).max():.2e}, max |dv| {dv.max():.2e}")
+    assert np.all(dx <= 2e-6 * (np.abs(x_ref) + 1.0))
+    assert np.all(dv <= 2e-6 * (np.abs(v_ref) + 1.0))
 
 
 def test_time_reversibility():
@@ -154,8 +158,12 @@ def test_time_reversibility():
     for _ in range(10):
         nb.kdk_step(pm, vel, acc, G, eps2, dt)
     torch.cuda.synchronize()
-    assert np.abs(pm.cpu().numpy()[:, :3] - pm0[:, :3]).max() <= 1e-5
-    assert np.abs(-vel.cpu().numpy()[:, :3] - v0[:, :3]).max() <= 1e-4
+    x0 = pm0[:, :3].astype(np.float64)
+    dx = np.abs(pm.cpu().numpy()[:, :3] - x0)
+    dv = np.abs(-vel.cpu().numpy()[:, :3] - v0[:, :3])
+    log(f"reversibility: max |dx|/(|x|+1) {(dx / (np.abs(x0) + 1)).max():.2e}, max |dv| {dv.max():.2e}")
+    assert np.all(dx <= 4e-6 * (np.abs(x0) + 1.0))
+    assert dv.max() <= 1e-5
 
 
 def test_collision1m_twenty_steps():
