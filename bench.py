@@ -95,6 +95,50 @@ def cpu_baseline(pm_np, acc0_np, w, seconds):
     }
 
 
+SPLITJ_CHUNKS = (32, 256, 1024, 4096, 16384)
+SPLITJ_MAX_WORKSPACE = 16 << 30
+
+
+def _time(torch, fn, reps):
+    stream = torch.cuda.current_stream()
+    fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def _sweep_line(w, ms, **kw):
+    inter = float(w.n) * float(w.n)
+    best = min(ms)
+    tflops = FLOPS_PER_INTERACTION * inter / (best * 1e-3) / 1e12
+    print(json.dumps({"workload": w.name, "n": w.n, **kw, "ms_min": best,
+                      "ms_avg": sum(ms) / len(ms),
+                      "interactions_per_s_billions": inter / (best * 1e-3) / 1e9,
+                      "pct_fp32_peak": 100 * tflops / PEAK_FP32_TFLOPS}), flush=True)
+
+
+def sweep(nb, torch, w, pm, acc, reps):
+    """Force-pass time of every compiled variant on the workload, then of the
+    two-pass split-j decomposition for a range of chunk widths (workspace
+    permitting)."""
+    for v in range(nb.nbody_accel_variant_count()):
+        ms = _time(torch, lambda: nb.nbody_accel_variant(pm, w.G, w.eps2, acc, v), reps)
+        _sweep_line(w, ms, variant=v, tiling=nb.nbody_accel_variant_info(v))
+    for j_chunk in SPLITJ_CHUNKS:
+        need = nb.nbody_accel_splitj_workspace_bytes(w.n, j_chunk)
+        if need > SPLITJ_MAX_WORKSPACE or -(-w.n // j_chunk) > 65535:
+            continue
+        ws = torch.empty(need, dtype=torch.uint8, device=pm.device)
+        ms = _time(torch, lambda: nb.nbody_accel_splitj(pm, w.G, w.eps2, acc, j_chunk, ws), reps)
+        _sweep_line(w, ms, splitj_chunk=j_chunk, workspace_bytes=need)
+        del ws
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -105,6 +149,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target length of the oracle CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the force pass of every compiled variant (one JSON line each) "
+                         "instead of the step benchmark")
+    ap.add_argument("--reps", type=int, default=3, help="timed force passes per variant (--sweep)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -131,6 +179,9 @@ def main():
     pm = torch.from_numpy(pm_np).to(dev)
     vel = torch.from_numpy(vel_np).to(dev)
     acc = torch.empty_like(pm)
+    if args.sweep:
+        sweep(nb, torch, w, pm, acc, args.reps)
+        return
     variant = args.variant if args.variant is not None else nb.nbody_accel_variant_for_n(w.n)
     info = nb.nbody_accel_variant_info(variant)
 

@@ -25,17 +25,19 @@
 
 namespace nbody {
 
-template <int K, int T, int WAVES, int S, int U, class L>
-__global__ __launch_bounds__(WAVES *kWave) void force_tile_kernel(L lay, int n, int n_tiles,
-                                                                  int tiles_per_part, float G,
-                                                                  float eps2) {
+// OCC > 0 asks the compiler to fit OCC waves per SIMD (it then caps VGPRs at
+// 512 / OCC); 0 leaves the register budget to the compiler.
+template <int K, int T, int WAVES, int S, int U, int OCC, class L>
+__global__ __launch_bounds__(WAVES *kWave)
+__attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1))) void force_tile_kernel(
+    L lay, int n, int n_tiles, int tiles_per_part, float G, float eps2) {
   constexpr int GW = WAVES / S;            // i-groups (waves) per part
   constexpr int NTHREADS = WAVES * kWave;  // threads per block
   constexpr int LOADS = (S * T) / NTHREADS;
   static_assert(WAVES % S == 0, "waves must be a multiple of the split");
   static_assert((S * T) % NTHREADS == 0, "staged bodies must divide evenly over threads");
-  static_assert((S - 1) * GW * K * 3 * kWave <= 2 * S * T * 4,
-                "part-combine scratch must fit in the tile buffers");
+  static_assert(S == 1 || GW * K * 3 * kWave <= 2 * S * T * 4,
+                "one part's sums must fit in the tile buffers");
   __shared__ float4 tile[2][S * T];
 
   const int tid = threadIdx.x;
@@ -115,23 +117,25 @@ __global__ __launch_bounds__(WAVES *kWave) void force_tile_kernel(L lay, int n, 
   }
 
   if constexpr (S > 1) {
-    __syncthreads();  // every wave is done with the tiles; reuse them
+    // Part p's sums go through the (now idle) tile buffer one part at a time
+    // and part 0 adds them in ascending p.
     float *red = reinterpret_cast<float *>(&tile[0][0]);
-    if (part > 0) {
-#pragma unroll
-      for (int q = 0; q < K; ++q) {
-        const int o = ((((part - 1) * GW + grp) * K + q) * 3) * kWave + lane;
-        red[o] = ax[q];
-        red[o + kWave] = ay[q];
-        red[o + 2 * kWave] = az[q];
-      }
-    }
-    __syncthreads();
-    if (part == 0) {
-      for (int p = 1; p < S; ++p) {
+    for (int p = 1; p < S; ++p) {
+      __syncthreads();
+      if (part == p) {
 #pragma unroll
         for (int q = 0; q < K; ++q) {
-          const int o = ((((p - 1) * GW + grp) * K + q) * 3) * kWave + lane;
+          const int o = ((grp * K + q) * 3) * kWave + lane;
+          red[o] = ax[q];
+          red[o + kWave] = ay[q];
+          red[o + 2 * kWave] = az[q];
+        }
+      }
+      __syncthreads();
+      if (part == 0) {
+#pragma unroll
+        for (int q = 0; q < K; ++q) {
+          const int o = ((grp * K + q) * 3) * kWave + lane;
           ax[q] += red[o];
           ay[q] += red[o + kWave];
           az[q] += red[o + 2 * kWave];
@@ -149,37 +153,45 @@ __global__ __launch_bounds__(WAVES *kWave) void force_tile_kernel(L lay, int n, 
   }
 }
 
-template <int K, int T, int WAVES, int S, int U, class L>
+template <int K, int T, int WAVES, int S, int U, int OCC, class L>
 static hipError_t launch_tile(const L &lay, int n, float G, float eps2, hipStream_t stream) {
   constexpr int GW = WAVES / S;
   const int per_block = GW * kWave * K;
   const int blocks = (n + per_block - 1) / per_block;
   const int n_tiles = (n + T - 1) / T;
   const int tiles_per_part = (n_tiles + S - 1) / S;
-  hipLaunchKernelGGL((force_tile_kernel<K, T, WAVES, S, U, L>), dim3(blocks),
+  hipLaunchKernelGGL((force_tile_kernel<K, T, WAVES, S, U, OCC, L>), dim3(blocks),
                      dim3(WAVES * kWave), 0, stream, lay, n, n_tiles, tiles_per_part, G, eps2);
   return hipGetLastError();
 }
 
-// (id, K, T, waves, S, unroll).  Ids are part of the ABI (nbody_accel_variant).
-#define NBODY_FORCE_VARIANTS(X) \
-  X(0, 1, 256, 4, 1, 4)         \
-  X(1, 2, 256, 4, 1, 4)         \
-  X(2, 4, 256, 4, 1, 4)         \
-  X(3, 8, 256, 4, 1, 2)         \
-  X(4, 4, 512, 4, 1, 4)         \
-  X(5, 8, 512, 4, 1, 2)         \
-  X(6, 4, 256, 4, 1, 1)         \
-  X(7, 4, 256, 4, 1, 8)         \
-  X(8, 1, 256, 8, 2, 4)         \
-  X(9, 2, 256, 8, 2, 4)         \
-  X(10, 1, 256, 16, 4, 4)       \
-  X(11, 1, 64, 16, 16, 4)       \
-  X(12, 2, 128, 16, 8, 4)       \
-  X(13, 4, 256, 8, 2, 4)
+// (id, K, T, waves, S, unroll, occupancy target).  Ids are part of the ABI
+// (nbody_accel_variant).  Waves per SIMD at n = 2^20 are noted for the
+// large-n rows (1024 SIMDs; at most 8 waves resident per SIMD).
+#define NBODY_FORCE_VARIANTS(X)  \
+  X(0, 1, 256, 4, 1, 4, 0)       /* 4096 blocks, 16 waves/SIMD (two rounds) */ \
+  X(1, 2, 256, 4, 1, 4, 0)       /* 2048 blocks, 8 waves/SIMD */               \
+  X(2, 4, 256, 4, 1, 4, 0)       /* 1024 blocks, 4 waves/SIMD */               \
+  X(3, 8, 256, 4, 1, 2, 0)       /* 512 blocks, 2 waves/SIMD */                \
+  X(4, 4, 512, 4, 1, 4, 0)                                                     \
+  X(5, 2, 512, 4, 1, 4, 0)                                                     \
+  X(6, 4, 256, 4, 1, 1, 0)                                                     \
+  X(7, 4, 256, 4, 1, 8, 0)                                                     \
+  X(8, 1, 256, 8, 2, 4, 0)                                                     \
+  X(9, 2, 256, 8, 2, 4, 0)                                                     \
+  X(10, 1, 256, 16, 4, 4, 0)                                                   \
+  X(11, 1, 64, 16, 16, 4, 0)     /* small n: 64 i per block */                 \
+  X(12, 2, 128, 16, 8, 4, 0)     /* small n: 128 i per block */                \
+  X(13, 4, 256, 8, 2, 1, 8)      /* 1024 blocks x 8 waves: 8 waves/SIMD */     \
+  X(14, 4, 256, 8, 2, 2, 8)                                                    \
+  X(15, 2, 256, 4, 1, 4, 8)                                                    \
+  X(16, 2, 256, 8, 2, 4, 8)      /* 1024 blocks x 8 waves */                   \
+  X(17, 8, 256, 16, 4, 2, 4)     /* 512 blocks x 16 waves, 4+ waves/SIMD */    \
+  X(18, 4, 512, 8, 2, 2, 8)                                                    \
+  X(19, 2, 512, 8, 1, 4, 8)      /* 1024 i per block, 1024 blocks x 8 waves */
 
 static const ForceVariant kVariants[] = {
-#define X(id, K, T, W, S, U) {K, T, W, S, U},
+#define X(id, K, T, W, S, U, OCC) {K, T, W, S, U},
     NBODY_FORCE_VARIANTS(X)
 #undef X
 };
@@ -190,23 +202,22 @@ const ForceVariant *force_variant(int v) {
   return (v >= 0 && v < force_variant_count()) ? &kVariants[v] : nullptr;
 }
 
-// Chooses a variant that gives the chip (256 CUs x 4 SIMDs) at least ~2
-// wavefronts per SIMD where n allows, with the most i-bodies per lane that
-// still does so.
+// Measured on MI355X (force-pass sweeps over every variant): small and
+// medium n want one body per lane and a 16-way j split, so that every SIMD
+// holds several waves; from a few hundred thousand bodies on, two bodies per
+// lane in 8-wave blocks (two j parts) with a VGPR budget that fits 8 waves
+// per SIMD is fastest.
 int force_variant_for_n(int64_t n) {
-  if (n <= 32768) return 11;   // 64 i per block, j split 16 ways
-  if (n <= 131072) return 12;  // 128 i per block, j split 8 ways
-  if (n <= 262144) return 9;   // 512 i per block, j split 2 ways
-  if (n <= 524288) return 1;   // 512 i per block
-  return 2;                    // 1024 i per block
+  if (n <= 200000) return 11;  // 64 i per block, j split 16 ways
+  return 16;                   // 512 i per block, j split 2 ways, 8 waves/SIMD
 }
 
 template <class L>
 static hipError_t dispatch(int v, const L &lay, int n, float G, float eps2, hipStream_t stream) {
   switch (v) {
-#define X(id, K, T, W, S, U) \
-  case id:                   \
-    return launch_tile<K, T, W, S, U>(lay, n, G, eps2, stream);
+#define X(id, K, T, W, S, U, OCC) \
+  case id:                        \
+    return launch_tile<K, T, W, S, U, OCC>(lay, n, G, eps2, stream);
     NBODY_FORCE_VARIANTS(X)
 #undef X
     default:
