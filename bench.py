@@ -21,7 +21,6 @@ bounded sample of the same workload's rows on the host cores.
 Prints one JSON line on stdout; progress goes to stderr.
 """
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -34,20 +33,10 @@ FLOPS_PER_INTERACTION = 20          # "Cuda Nbody Notes", pair-step comments
 PEAK_FP32_TFLOPS = 157.3            # MI355X FP32 vector, 256 CU x 64 lanes x 2 x 2 x 2.4 GHz
 METRIC = "body-body interactions/s (billions), N=1M fp32; % of MI355X FP32 VALU peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "force_plummer1m_traffic.json")
-KERNEL_SOURCES = ("direct_all_pairs_softened_amd/csrc/force.hip",
-                  "direct_all_pairs_softened_amd/csrc/nbody_common.hpp")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
-
-
-def kernel_source_hash():
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 def traffic_per_launch():
@@ -58,6 +47,7 @@ def traffic_per_launch():
             t = json.load(f)
     except (OSError, ValueError):
         return None
+    from direct_all_pairs_softened_amd.counters import kernel_source_hash
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None
     return t.get("hbm_bytes_per_launch")

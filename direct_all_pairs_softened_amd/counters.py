@@ -1,0 +1,171 @@
+"""Hardware-counter runs of the force pass (run under rocprofv3 --pmc).
+
+``run``: one calibration copy of a known number of bytes (torch's copy
+kernel, HBM to HBM), then one force pass of a workload.  Profile it once per
+counter group, e.g.
+
+    rocprofv3 --pmc FETCH_SIZE -d DIR/fetch -o run -- \\
+        python3 -m direct_all_pairs_softened_amd.counters run --workload plummer1m
+
+``summarize``: reads the counter_collection CSVs of those runs and writes a
+JSON record (HBM bytes per force launch, scaled by what the same counters
+read for the copy) and a Markdown table.
+
+FETCH_SIZE and WRITE_SIZE are in KiB per dispatch; each is scaled by
+copy_bytes / (counter reading of the copy), so a counter that over- or
+under-counts by a constant factor is corrected.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+COPY_BYTES = 1 << 30
+FORCE_KERNEL = "force_tile_kernel"
+COPY_KERNEL_HINTS = ("copyBuffer", "copy", "Copy")
+KERNEL_SOURCES = ("direct_all_pairs_softened_amd/csrc/force.hip",
+                  "direct_all_pairs_softened_amd/csrc/nbody_common.hpp")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def cmd_run(args):
+    sys.path.insert(0, ROOT)
+    import torch
+
+    import direct_all_pairs_softened_amd as nb
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    pm_np, _ = workloads.make(w.name)
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)          # device-to-device copy of COPY_BYTES
+    torch.cuda.synchronize()
+    pm = torch.from_numpy(pm_np).to(dev)
+    acc = torch.empty_like(pm)
+    v = args.variant if args.variant is not None else nb.nbody_accel_variant_for_n(w.n)
+    nb.nbody_accel_variant(pm, w.G, w.eps2, acc, v)
+    torch.cuda.synchronize()
+    print(f"counters run: copy {COPY_BYTES} B, force variant {v} on {w.name}", flush=True)
+
+
+def read_counters(pattern):
+    """{(dispatch_id, kernel_name): {counter: summed value}} from counter CSVs."""
+    out = defaultdict(lambda: defaultdict(float))
+    files = glob.glob(pattern, recursive=True)
+    if not files:
+        raise FileNotFoundError(pattern)
+    for path in files:
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                key = (int(row["Dispatch_Id"]), row["Kernel_Name"])
+                out[key][row["Counter_Name"]] += float(row["Counter_Value"])
+    return out
+
+
+def pick(rows, hint_list):
+    for (did, name), vals in sorted(rows.items()):
+        if any(h in name for h in hint_list):
+            return name, vals
+    raise KeyError(f"no kernel matching {hint_list}")
+
+
+def cmd_summarize(args):
+    fetch = read_counters(os.path.join(args.fetch_dir, "**", "*counter_collection.csv"))
+    write = read_counters(os.path.join(args.write_dir, "**", "*counter_collection.csv"))
+    copy_name, cf = pick(fetch, COPY_KERNEL_HINTS)
+    kname, ff = pick(fetch, (FORCE_KERNEL,))
+    _, cw = pick(write, COPY_KERNEL_HINTS)
+    _, fw = pick(write, (FORCE_KERNEL,))
+    fetch_scale = COPY_BYTES / (cf["FETCH_SIZE"] * 1024.0)
+    write_scale = COPY_BYTES / (cw["WRITE_SIZE"] * 1024.0)
+    force_fetch = ff["FETCH_SIZE"] * 1024.0 * fetch_scale
+    force_write = fw["WRITE_SIZE"] * 1024.0 * write_scale
+    rec = {
+        "workload": args.workload,
+        "n": args.n,
+        "kernel": kname,
+        "kernel_source_hash": kernel_source_hash(),
+        "copy_kernel": copy_name,
+        "copy_bytes": COPY_BYTES,
+        "copy_fetch_kib": cf["FETCH_SIZE"],
+        "copy_write_kib": cw["WRITE_SIZE"],
+        "fetch_scale": fetch_scale,
+        "write_scale": write_scale,
+        "force_fetch_kib": ff["FETCH_SIZE"],
+        "force_write_kib": fw["WRITE_SIZE"],
+        "hbm_bytes_per_launch": force_fetch + force_write,
+        "algorithmic_bytes_per_launch": 32 * args.n,
+    }
+    if args.sq_dir:
+        sq = read_counters(os.path.join(args.sq_dir, "**", "*counter_collection.csv"))
+        _, fs = pick(sq, (FORCE_KERNEL,))
+        rec["sq"] = dict(fs)
+    if args.dram_dir:
+        dr = read_counters(os.path.join(args.dram_dir, "**", "*counter_collection.csv"))
+        _, fd = pick(dr, (FORCE_KERNEL,))
+        _, cd = pick(dr, COPY_KERNEL_HINTS)
+        rec["tcc"] = {"force": dict(fd), "copy": dict(cd)}
+    with open(args.out_json, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(rec, indent=1, sort_keys=True))
+
+
+def cmd_trace_report(args):
+    """Markdown table of a rocprofv3 --stats kernel_stats.csv."""
+    files = glob.glob(os.path.join(args.dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(args.dir)
+    lines = ["| kernel | calls | avg ms | min ms | max ms | % time |",
+             "|---|---|---|---|---|---|"]
+    with open(files[0], newline="") as f:
+        for row in csv.DictReader(f):
+            name = row["Name"]
+            if len(name) > 90:
+                name = name[:87] + "..."
+            lines.append("| `%s` | %s | %.4f | %.4f | %.4f | %.2f |" % (
+                name, row["Calls"], float(row["AverageNs"]) / 1e6,
+                float(row["MinNs"]) / 1e6, float(row["MaxNs"]) / 1e6,
+                float(row["Percentage"])))
+    print("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    r = sub.add_parser("run")
+    r.add_argument("--workload", default="plummer1m")
+    r.add_argument("--variant", type=int, default=None)
+    s = sub.add_parser("summarize")
+    s.add_argument("--fetch-dir", required=True)
+    s.add_argument("--write-dir", required=True)
+    s.add_argument("--sq-dir", default=None)
+    s.add_argument("--dram-dir", default=None)
+    s.add_argument("--workload", default="plummer1m")
+    s.add_argument("--n", type=int, default=1 << 20)
+    s.add_argument("--out-json", required=True)
+    t = sub.add_parser("trace-report")
+    t.add_argument("--dir", required=True)
+    a = ap.parse_args()
+    {"run": cmd_run, "summarize": cmd_summarize, "trace-report": cmd_trace_report}[a.cmd](a)
+
+
+if __name__ == "__main__":
+    main()
