@@ -112,14 +112,23 @@ def _sweep_line(w, ms, **kw):
                       "pct_fp32_peak": 100 * tflops / PEAK_FP32_TFLOPS}), flush=True)
 
 
-def sweep(nb, torch, w, pm, acc, reps):
+def sweep(nb, torch, w, pm, acc, reps, paths):
     """Force-pass time of every compiled variant on the workload, then of the
     two-pass split-j decomposition for a range of chunk widths (workspace
     permitting)."""
-    for v in range(nb.nbody_accel_variant_count()):
+    for v in range(nb.nbody_accel_variant_count() if "tile" in paths else 0):
         ms = _time(torch, lambda: nb.nbody_accel_variant(pm, w.G, w.eps2, acc, v), reps)
         _sweep_line(w, ms, variant=v, tiling=nb.nbody_accel_variant_info(v))
-    for j_chunk in SPLITJ_CHUNKS:
+    for v in range(nb.nbody_accel_symmetric_variant_count() if "symmetric" in paths else 0):
+        need = nb.nbody_accel_symmetric_workspace_bytes(w.n, v)
+        if need > 4 * SPLITJ_MAX_WORKSPACE:
+            continue
+        ws = torch.empty(need, dtype=torch.uint8, device=pm.device)
+        ms = _time(torch, lambda: nb.nbody_accel_symmetric(pm, w.G, w.eps2, acc, ws, v), reps)
+        _sweep_line(w, ms, symmetric_variant=v, panel=nb.nbody_accel_symmetric_panel(v),
+                    workspace_bytes=need)
+        del ws
+    for j_chunk in SPLITJ_CHUNKS if "splitj" in paths else ():
         need = nb.nbody_accel_splitj_workspace_bytes(w.n, j_chunk)
         if need > SPLITJ_MAX_WORKSPACE or -(-w.n // j_chunk) > 65535:
             continue
@@ -135,6 +144,9 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="plummer1m")
+    ap.add_argument("--path", choices=("tile", "symmetric"), default="symmetric",
+                    help="force pass: one-sided LDS-tiled (nbody_accel) or pair-symmetric "
+                         "(nbody_accel_symmetric)")
     ap.add_argument("--variant", type=int, default=None, help="force a compiled force variant")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target length of the oracle CPU-baseline sample")
@@ -143,6 +155,8 @@ def main():
                     help="time the force pass of every compiled variant (one JSON line each) "
                          "instead of the step benchmark")
     ap.add_argument("--reps", type=int, default=3, help="timed force passes per variant (--sweep)")
+    ap.add_argument("--sweep-paths", default="tile,symmetric,splitj",
+                    help="comma-separated subset of tile, symmetric, splitj (--sweep)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -170,13 +184,24 @@ def main():
     vel = torch.from_numpy(vel_np).to(dev)
     acc = torch.empty_like(pm)
     if args.sweep:
-        sweep(nb, torch, w, pm, acc, args.reps)
+        sweep(nb, torch, w, pm, acc, args.reps, set(args.sweep_paths.split(",")))
         return
-    variant = args.variant if args.variant is not None else nb.nbody_accel_variant_for_n(w.n)
-    info = nb.nbody_accel_variant_info(variant)
+    if args.path == "symmetric":
+        variant = (args.variant if args.variant is not None
+                   else nb.nbody_accel_symmetric_variant_for_n(w.n))
+        ws_bytes = nb.nbody_accel_symmetric_workspace_bytes(w.n, variant)
+        sym_ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        info = {"path": "symmetric", "panel": nb.nbody_accel_symmetric_panel(variant),
+                "workspace_bytes": ws_bytes}
 
-    def force():
-        nb.nbody_accel_variant(pm, w.G, w.eps2, acc, variant)
+        def force():
+            nb.nbody_accel_symmetric(pm, w.G, w.eps2, acc, sym_ws, variant)
+    else:
+        variant = args.variant if args.variant is not None else nb.nbody_accel_variant_for_n(w.n)
+        info = dict(nb.nbody_accel_variant_info(variant), path="tile")
+
+        def force():
+            nb.nbody_accel_variant(pm, w.G, w.eps2, acc, variant)
 
     force()
     torch.cuda.synchronize()

@@ -28,9 +28,10 @@ from collections import defaultdict
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 COPY_BYTES = 1 << 30
-FORCE_KERNEL = "force_tile_kernel"
+FORCE_KERNELS = ("symmetric_task_kernel", "force_tile_kernel")
 COPY_KERNEL_HINTS = ("copyBuffer", "copy", "Copy")
 KERNEL_SOURCES = ("direct_all_pairs_softened_amd/csrc/force.hip",
+                  "direct_all_pairs_softened_amd/csrc/symmetric.hip",
                   "direct_all_pairs_softened_amd/csrc/nbody_common.hpp")
 
 
@@ -59,10 +60,17 @@ def cmd_run(args):
     torch.cuda.synchronize()
     pm = torch.from_numpy(pm_np).to(dev)
     acc = torch.empty_like(pm)
-    v = args.variant if args.variant is not None else nb.nbody_accel_variant_for_n(w.n)
-    nb.nbody_accel_variant(pm, w.G, w.eps2, acc, v)
+    if args.path == "symmetric":
+        v = args.variant if args.variant is not None else nb.nbody_accel_symmetric_variant_for_n(w.n)
+        ws = torch.empty(nb.nbody_accel_symmetric_workspace_bytes(w.n, v), dtype=torch.uint8,
+                         device=dev)
+        nb.nbody_accel_symmetric(pm, w.G, w.eps2, acc, ws, v)
+    else:
+        v = args.variant if args.variant is not None else nb.nbody_accel_variant_for_n(w.n)
+        nb.nbody_accel_variant(pm, w.G, w.eps2, acc, v)
     torch.cuda.synchronize()
-    print(f"counters run: copy {COPY_BYTES} B, force variant {v} on {w.name}", flush=True)
+    print(f"counters run: copy {COPY_BYTES} B, {args.path} force variant {v} on {w.name}",
+          flush=True)
 
 
 def read_counters(pattern):
@@ -86,13 +94,23 @@ def pick(rows, hint_list):
     raise KeyError(f"no kernel matching {hint_list}")
 
 
+def algorithmic_bytes(kernel_name: str, n: int, panel: int) -> int:
+    """One-sided pass: 16 B read + 16 B written per body.  Pair-symmetric task
+    kernel: 16 B read per body plus its P^2 panel sums of 3 floats per body
+    (12 n P bytes, P = ceil(n / panel)), which the reduce kernel reads back."""
+    if "symmetric_task_kernel" in kernel_name:
+        P = -(-n // panel)
+        return 16 * n + 12 * P * P * panel
+    return 32 * n
+
+
 def cmd_summarize(args):
     fetch = read_counters(os.path.join(args.fetch_dir, "**", "*counter_collection.csv"))
     write = read_counters(os.path.join(args.write_dir, "**", "*counter_collection.csv"))
     copy_name, cf = pick(fetch, COPY_KERNEL_HINTS)
-    kname, ff = pick(fetch, (FORCE_KERNEL,))
+    kname, ff = pick(fetch, FORCE_KERNELS)
     _, cw = pick(write, COPY_KERNEL_HINTS)
-    _, fw = pick(write, (FORCE_KERNEL,))
+    _, fw = pick(write, FORCE_KERNELS)
     fetch_scale = COPY_BYTES / (cf["FETCH_SIZE"] * 1024.0)
     write_scale = COPY_BYTES / (cw["WRITE_SIZE"] * 1024.0)
     force_fetch = ff["FETCH_SIZE"] * 1024.0 * fetch_scale
@@ -111,15 +129,15 @@ def cmd_summarize(args):
         "force_fetch_kib": ff["FETCH_SIZE"],
         "force_write_kib": fw["WRITE_SIZE"],
         "hbm_bytes_per_launch": force_fetch + force_write,
-        "algorithmic_bytes_per_launch": 32 * args.n,
+        "algorithmic_bytes_per_launch": algorithmic_bytes(kname, args.n, args.panel),
     }
     if args.sq_dir:
         sq = read_counters(os.path.join(args.sq_dir, "**", "*counter_collection.csv"))
-        _, fs = pick(sq, (FORCE_KERNEL,))
+        _, fs = pick(sq, FORCE_KERNELS)
         rec["sq"] = dict(fs)
     if args.dram_dir:
         dr = read_counters(os.path.join(args.dram_dir, "**", "*counter_collection.csv"))
-        _, fd = pick(dr, (FORCE_KERNEL,))
+        _, fd = pick(dr, FORCE_KERNELS)
         _, cd = pick(dr, COPY_KERNEL_HINTS)
         rec["tcc"] = {"force": dict(fd), "copy": dict(cd)}
     with open(args.out_json, "w") as f:
@@ -153,6 +171,7 @@ def main():
     r = sub.add_parser("run")
     r.add_argument("--workload", default="plummer1m")
     r.add_argument("--variant", type=int, default=None)
+    r.add_argument("--path", choices=("tile", "symmetric"), default="symmetric")
     s = sub.add_parser("summarize")
     s.add_argument("--fetch-dir", required=True)
     s.add_argument("--write-dir", required=True)
@@ -160,6 +179,7 @@ def main():
     s.add_argument("--dram-dir", default=None)
     s.add_argument("--workload", default="plummer1m")
     s.add_argument("--n", type=int, default=1 << 20)
+    s.add_argument("--panel", type=int, default=2048)
     s.add_argument("--out-json", required=True)
     t = sub.add_parser("trace-report")
     t.add_argument("--dir", required=True)

@@ -178,6 +178,48 @@ int nbody_accel_splitj(const float *posmass, int64_t n, float G, float eps2, flo
                                          workspace, as_stream(stream)));
 }
 
+static int sym_variant(int v, int64_t n) { return v < 0 ? nbody::symmetric_variant_for_n(n) : v; }
+
+int nbody_accel_symmetric_variant_count(void) { return nbody::symmetric_variant_count(); }
+
+int nbody_accel_symmetric_variant_for_n(int64_t n) { return nbody::symmetric_variant_for_n(n); }
+
+int nbody_accel_symmetric_panel(int variant) {
+  if (variant < 0) return NBODY_ERR_INVALID_ARG;
+  const int v = variant;
+  if (v >= nbody::symmetric_variant_count()) return NBODY_ERR_INVALID_ARG;
+  return nbody::symmetric_panel(v);
+}
+
+size_t nbody_accel_symmetric_workspace_bytes(int64_t n, int variant) {
+  const int v = sym_variant(variant, n);
+  if (!n_ok(n) || v >= nbody::symmetric_variant_count()) return 0;
+  return nbody::symmetric_workspace_bytes(n, v);
+}
+
+int nbody_accel_symmetric(const float *posmass, int64_t n, float G, float eps2,
+                          float *accel_out, int variant, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  const int v = sym_variant(variant, n);
+  if (!n_ok(n)) return NBODY_ERR_INVALID_ARG;
+  if (int s = check_consts(G, eps2)) return s;
+  if (v >= nbody::symmetric_variant_count()) return NBODY_ERR_INVALID_ARG;
+  if (n == 0) return NBODY_OK;
+  const int64_t P = nbody::symmetric_panels(n, v);
+  if (P * (P + 1) / 2 > INT32_MAX) return NBODY_ERR_INVALID_ARG;
+  if (!posmass || !accel_out) return NBODY_ERR_INVALID_ARG;
+  if (!aligned(posmass, 16) || !aligned(accel_out, 16)) return NBODY_ERR_ALIGNMENT;
+  const size_t need = nbody::symmetric_workspace_bytes(n, v);
+  if (!workspace || workspace_bytes < need) return NBODY_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return NBODY_ERR_ALIGNMENT;
+  const size_t bytes = (size_t)n * 16;
+  if (overlap(posmass, bytes, accel_out, bytes) || overlap(workspace, need, posmass, bytes) ||
+      overlap(workspace, need, accel_out, bytes))
+    return NBODY_ERR_ALIAS;
+  return hip_status(nbody::launch_symmetric(posmass, (int)n, G, eps2, accel_out, v, workspace,
+                                            as_stream(stream)));
+}
+
 int nbody_leapfrog_step(float *posmass, float *vel, const float *accel, float dt, int64_t n,
                         void *stream) {
   if (!n_ok(n) || !isfinite(dt)) return NBODY_ERR_INVALID_ARG;

@@ -48,6 +48,15 @@ size_t splitj_workspace_bytes(int64_t n, int64_t j_chunk);
 hipError_t launch_splitj(const float *posmass, int n, float G, float eps2, float *accel,
                          int j_chunk, void *workspace, hipStream_t stream);
 
+// Pair-symmetric force pass (each pair once, applied to both bodies).
+int symmetric_variant_count();
+int symmetric_variant_for_n(int64_t n);
+int symmetric_panel(int v);
+int64_t symmetric_panels(int64_t n, int v);
+size_t symmetric_workspace_bytes(int64_t n, int v);
+hipError_t launch_symmetric(const float *posmass, int n, float G, float eps2, float *accel,
+                            int v, void *workspace, hipStream_t stream);
+
 // Integrator.
 hipError_t launch_leapfrog(float *posmass, float *vel, const float *accel, float dt, int n,
                            hipStream_t stream);

@@ -1,0 +1,264 @@
+// Pair-symmetric force pass: every unordered pair of bodies is evaluated
+// once and its term goes to both bodies (Newton's third law: the term on j
+// from i is the term on i from j times -m_i/m_j).  The atomics tutorial (CUDA
+// programming part 9, its neighbour-list example) runs the same symmetric
+// half loop but has to add the second body's share with atomicAdd.  Here the
+// share is carried in registers and added in a fixed order, so the result is
+// bitwise reproducible and there are no atomics.
+//
+// Decomposition.  Bodies are cut into P panels of B = 64 * W * K bodies (the
+// tail padded with zero-mass copies of the last body).  A block takes one
+// task (I, J), I <= J, of the P(P+1)/2 panel pairs:
+//  - wave w holds K bodies of panel I per lane in registers (its i-group);
+//  - panel J is walked in sweeps of 64 * KP bodies.  For a sweep each lane
+//    loads KP j-bodies, then 64 steps each evaluate the lane's K x KP pairs
+//    and rotate the j-state (x, y, z, m and the j-side sums) one lane along
+//    the wave with a DPP wave_ror:1 move.  After 64 steps every j-body has
+//    met every i-body of the wave and its state is back in its home lane;
+//  - pair term: r = x_j - x_i, inv = rsq(|r|^2 + eps^2), w = inv^3;
+//    i gains m_j w r (register sum), j gains -m_i w r (rotating sum);
+//  - the W waves' j-side sums are added in ascending wave order through LDS.
+// Diagonal tasks (I = J) use the one-sided sum (j over the whole panel,
+// self term exactly 0) and no j-side sums.
+//
+// Output of a task: part[I][J] = panel I's sums from panel J and, for I < J,
+// part[J][I] = panel J's sums from panel I.  A second kernel forms
+// a_i = G * sum_{J = 0 .. P-1} part[I(i)][J][i], ascending J.
+// Workspace: part float[P][P][3][B], i.e. 12 N^2 / B bytes.
+//
+// Per pair (two interactions) a lane issues 16 FP32 VALU ops and one
+// v_rsq_f32, plus 7 / K DPP moves; the one-sided kernel issues 12 ops and one
+// v_rsq_f32 per interaction.
+#include <math.h>
+
+#include "nbody_common.hpp"
+#include "nbody_internal.hpp"
+
+namespace nbody {
+
+namespace {
+
+// Lane l receives lane l - 1's value (lane 0 receives lane 63's).
+__device__ __forceinline__ float rotate_lanes(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x13C, 0xf, 0xf, false));
+}
+
+template <int K, int KP, int W, bool DIAG>
+__device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, int I, int J,
+                                         int P, float eps2, float *__restrict__ part,
+                                         float (*csum)[KP][3][kWave]) {
+  constexpr int B = W * kWave * K;
+  constexpr int JG = kWave * KP;
+  constexpr int NG = B / JG;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid % kWave;
+
+  float xi[K], yi[K], zi[K], mi[K], ax[K], ay[K], az[K];
+#pragma unroll
+  for (int q = 0; q < K; ++q) {
+    const int i = I * B + wave * (kWave * K) + q * kWave + lane;
+    const float4 b = pm[i < n ? i : n - 1];
+    xi[q] = b.x;
+    yi[q] = b.y;
+    zi[q] = b.z;
+    mi[q] = i < n ? b.w : 0.0f;
+    ax[q] = 0.0f;
+    ay[q] = 0.0f;
+    az[q] = 0.0f;
+  }
+
+  for (int g = 0; g < NG; ++g) {
+    float xj[KP], yj[KP], zj[KP], mj[KP], cx[KP], cy[KP], cz[KP];
+#pragma unroll
+    for (int p = 0; p < KP; ++p) {
+      const int j = J * B + g * JG + p * kWave + lane;
+      const float4 b = pm[j < n ? j : n - 1];
+      xj[p] = b.x;
+      yj[p] = b.y;
+      zj[p] = b.z;
+      mj[p] = j < n ? b.w : 0.0f;
+      cx[p] = 0.0f;
+      cy[p] = 0.0f;
+      cz[p] = 0.0f;
+    }
+    for (int s = 0; s < kWave; ++s) {
+#pragma unroll
+      for (int p = 0; p < KP; ++p) {
+#pragma unroll
+        for (int q = 0; q < K; ++q) {
+          const float dx = xj[p] - xi[q];
+          const float dy = yj[p] - yi[q];
+          const float dz = zj[p] - zi[q];
+          float d2 = __builtin_fmaf(dx, dx, eps2);
+          d2 = __builtin_fmaf(dy, dy, d2);
+          d2 = __builtin_fmaf(dz, dz, d2);
+          const float inv = __builtin_amdgcn_rsqf(d2);
+          if constexpr (DIAG) {
+            const float sj = (mj[p] * inv) * (inv * inv);
+            ax[q] = __builtin_fmaf(sj, dx, ax[q]);
+            ay[q] = __builtin_fmaf(sj, dy, ay[q]);
+            az[q] = __builtin_fmaf(sj, dz, az[q]);
+          } else {
+            const float w = (inv * inv) * inv;
+            const float sj = mj[p] * w;
+            ax[q] = __builtin_fmaf(sj, dx, ax[q]);
+            ay[q] = __builtin_fmaf(sj, dy, ay[q]);
+            az[q] = __builtin_fmaf(sj, dz, az[q]);
+            const float si = mi[q] * w;
+            cx[p] = __builtin_fmaf(si, dx, cx[p]);
+            cy[p] = __builtin_fmaf(si, dy, cy[p]);
+            cz[p] = __builtin_fmaf(si, dz, cz[p]);
+          }
+        }
+        xj[p] = rotate_lanes(xj[p]);
+        yj[p] = rotate_lanes(yj[p]);
+        zj[p] = rotate_lanes(zj[p]);
+        mj[p] = rotate_lanes(mj[p]);
+        if constexpr (!DIAG) {
+          cx[p] = rotate_lanes(cx[p]);
+          cy[p] = rotate_lanes(cy[p]);
+          cz[p] = rotate_lanes(cz[p]);
+        }
+      }
+    }
+    if constexpr (!DIAG) {
+      // j-side sums of this sweep: add the W waves in ascending order
+#pragma unroll
+      for (int p = 0; p < KP; ++p) {
+        csum[wave][p][0][lane] = cx[p];
+        csum[wave][p][1][lane] = cy[p];
+        csum[wave][p][2][lane] = cz[p];
+      }
+      __syncthreads();
+      for (int e = tid; e < KP * 3 * kWave; e += W * kWave) {
+        const int p = e / (3 * kWave), c = (e / kWave) % 3, l = e % kWave;
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) sum += csum[w][p][c][l];
+        part[(((size_t)J * P + I) * 3 + c) * B + g * JG + p * kWave + l] = -sum;
+      }
+      __syncthreads();
+    }
+  }
+
+#pragma unroll
+  for (int q = 0; q < K; ++q) {
+    const int b = wave * (kWave * K) + q * kWave + lane;
+    float *row = part + ((size_t)I * P + J) * 3 * B + b;
+    row[0] = ax[q];
+    row[B] = ay[q];
+    row[2 * B] = az[q];
+  }
+}
+
+// One block per task; blockIdx.x = J (J + 1) / 2 + I enumerates I <= J.
+template <int K, int KP, int W, int OCC>
+__global__ __launch_bounds__(W *kWave) __attribute__((amdgpu_waves_per_eu(OCC))) void
+symmetric_task_kernel(const float4 *__restrict__ pm, int n, int P, float eps2,
+                      float *__restrict__ part) {
+  __shared__ float csum[W][KP][3][kWave];
+  const long long t = blockIdx.x;
+  long long J = (long long)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
+  while (J * (J + 1) / 2 > t) --J;
+  while ((J + 1) * (J + 2) / 2 <= t) ++J;
+  const int Jc = (int)J;
+  const int Ic = (int)(t - J * (J + 1) / 2);
+  if (Ic == Jc)
+    sym_task<K, KP, W, true>(pm, n, Ic, Jc, P, eps2, part, csum);
+  else
+    sym_task<K, KP, W, false>(pm, n, Ic, Jc, P, eps2, part, csum);
+}
+
+__global__ __launch_bounds__(256) void symmetric_reduce_kernel(const float *__restrict__ part,
+                                                               int n, int P, int B, float G,
+                                                               float4 *__restrict__ out) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int I = i / B, b = i % B;
+  const float *s = part + (size_t)I * P * 3 * B + b;
+  float sx = 0.0f, sy = 0.0f, sz = 0.0f;
+  for (int J = 0; J < P; ++J, s += (size_t)3 * B) {
+    sx += s[0];
+    sy += s[B];
+    sz += s[2 * B];
+  }
+  out[i] = make_float4(G * sx, G * sy, G * sz, 0.0f);
+}
+
+// (id, K, KP, waves, occupancy target); panel B = 64 * waves * K.
+#define NBODY_SYM_VARIANTS(X) \
+  X(0, 8, 2, 4, 4)            \
+  X(1, 8, 1, 4, 4)            \
+  X(2, 4, 2, 4, 6)            \
+  X(3, 8, 2, 8, 4)            \
+  X(4, 4, 4, 4, 4)            \
+  X(5, 8, 1, 8, 4)            \
+  X(6, 16, 1, 4, 2)           \
+  X(7, 12, 1, 4, 3)           \
+  X(8, 8, 1, 2, 4)            \
+  X(9, 8, 1, 4, 6)            \
+  X(10, 6, 1, 4, 5)           \
+  X(11, 16, 1, 2, 2)
+
+struct SymVariant {
+  int K, KP, W;
+};
+
+const SymVariant kSym[] = {
+#define X(id, K, KP, W, OCC) {K, KP, W},
+    NBODY_SYM_VARIANTS(X)
+#undef X
+};
+
+}  // namespace
+
+int symmetric_variant_count() { return (int)(sizeof(kSym) / sizeof(kSym[0])); }
+
+// Measured on MI355X (force-pass sweeps): 8 i-bodies and 1 j-body per lane
+// in 4-wave blocks is fastest at 1e5-1e6 bodies; 1024-body panels (2-wave
+// blocks) give more panel pairs at the low end, 2048-body panels halve the
+// workspace at the high end.  Below ~5e4 bodies there are too few panel pairs
+// to fill the chip and the one-sided nbody_accel is faster.
+int symmetric_variant_for_n(int64_t n) { return n <= 300000 ? 8 : 9; }
+
+int symmetric_panel(int v) { return kWave * kSym[v].W * kSym[v].K; }
+
+int64_t symmetric_panels(int64_t n, int v) {
+  const int64_t B = symmetric_panel(v);
+  return (n + B - 1) / B;
+}
+
+size_t symmetric_workspace_bytes(int64_t n, int v) {
+  if (n <= 0 || v < 0 || v >= symmetric_variant_count()) return 0;
+  const int64_t B = symmetric_panel(v), P = symmetric_panels(n, v);
+  return (size_t)P * (size_t)P * 3 * (size_t)B * sizeof(float);
+}
+
+hipError_t launch_symmetric(const float *posmass, int n, float G, float eps2, float *accel,
+                            int v, void *workspace, hipStream_t stream) {
+  const int B = symmetric_panel(v);
+  const int P = (int)symmetric_panels(n, v);
+  const long long tasks = (long long)P * (P + 1) / 2;
+  float *part = reinterpret_cast<float *>(workspace);
+  const float4 *pm = reinterpret_cast<const float4 *>(posmass);
+  switch (v) {
+#define X(id, K, KP, W, OCC)                                                              \
+  case id:                                                                                \
+    hipLaunchKernelGGL((symmetric_task_kernel<K, KP, W, OCC>), dim3((unsigned)tasks),     \
+                       dim3(W * kWave), 0, stream, pm, n, P, eps2, part);                 \
+    break;
+    NBODY_SYM_VARIANTS(X)
+#undef X
+    default:
+      return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(symmetric_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, part,
+                     n, P, B, G, reinterpret_cast<float4 *>(accel));
+  return hipGetLastError();
+}
+
+}  // namespace nbody

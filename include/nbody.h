@@ -129,6 +129,38 @@ int nbody_accel_splitj(const float *posmass, int64_t n, float G, float eps2,
  * j_chunk). */
 size_t nbody_accel_splitj_workspace_bytes(int64_t n, int64_t j_chunk);
 
+/* Pair-symmetric force pass: each unordered pair is evaluated once and its
+ * term is applied to both bodies (Newton's third law).  The atomics tutorial
+ * ("CUDA programming (9)", neighbour-list example) runs this symmetric half
+ * loop with atomicAdd for the second body; here the second body's share is
+ * carried in registers, rotated across the wavefront, and every sum has a
+ * fixed order, so the result is bitwise reproducible.  Bodies are grouped in
+ * panels of nbody_accel_symmetric_panel(variant) bodies; a panel pair (I, J)
+ * writes panel I's sums from J and panel J's sums from I into the
+ * workspace, and a second kernel adds, for each body, the P panel sums in
+ * ascending panel order and multiplies by G.  The order differs from
+ * nbody_accel's, so the two agree to rounding, not bitwise.
+ *   variant    0 <= variant < nbody_accel_symmetric_variant_count(), or -1
+ *              for the library's choice.
+ *   workspace  >= nbody_accel_symmetric_workspace_bytes(n, variant) bytes
+ *              (12 n^2 / panel bytes: about 6.4 GB at n = 2^20), 16-byte
+ *              aligned, disjoint from posmass and accel_out; contents on
+ *              return are unspecified.
+ * Other arguments as nbody_accel.  NBODY_ERR_INVALID_ARG also when the
+ * panel pairs exceed 2^31 - 1 (n beyond ~1.3e8). */
+int nbody_accel_symmetric(const float *posmass, int64_t n, float G, float eps2,
+                          float *accel_out, int variant, void *workspace,
+                          size_t workspace_bytes, void *stream);
+/* Workspace bytes for (n, variant); variant -1 means the library's choice
+ * for n.  0 for n == 0 or an unknown variant. */
+size_t nbody_accel_symmetric_workspace_bytes(int64_t n, int variant);
+/* Number of compiled variants of the pair-symmetric pass. */
+int nbody_accel_symmetric_variant_count(void);
+/* Panel size (bodies) of a variant; NBODY_ERR_INVALID_ARG if unknown. */
+int nbody_accel_symmetric_panel(int variant);
+/* The variant nbody_accel_symmetric uses for n when passed -1. */
+int nbody_accel_symmetric_variant_for_n(int64_t n);
+
 /* The force pass on other body layouts; same arithmetic and order as
  * nbody_accel for the same n, so the outputs are bitwise equal to its
  * (ax, ay, az).  README section 3.5 compares float4 against 12-byte float3

@@ -168,3 +168,28 @@ def test_binding_rejects_cpu_tensors():
     pm = torch.zeros(4, 4)
     with pytest.raises(ValueError):
         nb.nbody_accel(pm, 1.0, 1e-4, torch.zeros(4, 4))
+
+
+def test_symmetric_host_side(lib):
+    count = nb.nbody_accel_symmetric_variant_count()
+    assert count >= 1
+    for v in range(count):
+        panel = nb.nbody_accel_symmetric_panel(v)
+        assert panel > 0 and panel % 64 == 0
+        P = -(-1000 // panel)
+        assert nb.nbody_accel_symmetric_workspace_bytes(1000, v) == P * P * 3 * panel * 4
+    assert nb.nbody_accel_symmetric_panel(count) == nb.NBODY_ERR_INVALID_ARG
+    assert nb.nbody_accel_symmetric_workspace_bytes(0, 0) == 0
+    assert nb.nbody_accel_symmetric_workspace_bytes(1000, count) == 0
+    f = lib.nbody_accel_symmetric
+    need = nb.nbody_accel_symmetric_workspace_bytes(1000, 0)
+    assert f(vp(A), 0, 1.0, 1e-4, vp(B), 0, None, 0, None) == nb.NBODY_OK
+    assert f(vp(A), 1000, 1.0, 1e-4, vp(B), count, vp(C), need, None) == nb.NBODY_ERR_INVALID_ARG
+    assert f(vp(A), 1000, 1.0, 0.0, vp(B), 0, vp(C), need, None) == nb.NBODY_ERR_INVALID_ARG
+    assert f(vp(A), 1000, 1.0, 1e-4, vp(B), 0, vp(C), need - 4, None) == nb.NBODY_ERR_WORKSPACE
+    assert f(vp(A), 1000, 1.0, 1e-4, vp(B), 0, None, need, None) == nb.NBODY_ERR_WORKSPACE
+    assert f(vp(A), 1000, 1.0, 1e-4, vp(B), 0, vp(C + 4), need, None) == nb.NBODY_ERR_ALIGNMENT
+    assert f(vp(A), 1000, 1.0, 1e-4, vp(A), 0, vp(C), need, None) == nb.NBODY_ERR_ALIAS
+    assert f(vp(A), 1000, 1.0, 1e-4, vp(B), 0, vp(B - 64), need, None) == nb.NBODY_ERR_ALIAS
+    # more panel pairs than a grid holds
+    assert f(vp(A), nb.NBODY_MAX_N, 1.0, 1e-4, vp(B), 0, vp(C), 1 << 62, None) == nb.NBODY_ERR_INVALID_ARG

@@ -219,3 +219,80 @@ def test_collision1m_ragged_sampled():
     a = gpu_accel(pm, w.G, w.eps2)
     assert np.all(a[:, 3] == 0)
     assert_parity(a[rows], ref, "collision1m")
+
+
+# ---------------------------------------------------------------------------
+# Pair-symmetric path
+# ---------------------------------------------------------------------------
+
+def sym_accel(pm_np, G=1.0, eps2=1e-4, variant=-1):
+    t = torch.from_numpy(pm_np).to(DEV)
+    out = torch.full_like(t, float("nan"))
+    n = pm_np.shape[0]
+    ws = torch.empty(max(nb.nbody_accel_symmetric_workspace_bytes(n, variant), 16),
+                     dtype=torch.uint8, device=DEV)
+    nb.nbody_accel_symmetric(t, G, eps2, out, ws, variant)
+    torch.cuda.synchronize()
+    assert np.array_equal(t.cpu().numpy(), pm_np), "posmass was modified"
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 65, 1000, 2048, 2049, 5000])
+def test_symmetric_every_variant_small(n):
+    pm, _ = workloads.uniform_cube(n, seed=100 + n)
+    ref = ref_accel(pm)
+    for v in range(nb.nbody_accel_symmetric_variant_count()):
+        log(f"symmetric n={n} variant={v}")
+        a = sym_accel(pm, variant=v)
+        assert np.all(a[:, 3] == 0.0)
+        if n == 1:
+            assert np.array_equal(a, np.zeros((1, 4), F32))
+        else:
+            assert_parity(a, ref, f"symmetric n={n} v={v}")
+
+
+def test_symmetric_plummer16k_full_and_deterministic():
+    w = workloads.WORKLOADS["plummer16k"]
+    pm, _ = workloads.make("plummer16k")
+    ref = ref_accel(pm, w.G, w.eps2)
+    a = sym_accel(pm, w.G, w.eps2)
+    assert_parity(a, ref, "symmetric plummer16k")
+    assert np.array_equal(a, sym_accel(pm, w.G, w.eps2))
+    m = pm[:, 3].astype(np.float64)
+    ag = a[:, :3].astype(np.float64)
+    net = np.linalg.norm((m[:, None] * ag).sum(axis=0))
+    assert net / (m * np.linalg.norm(ag, axis=1)).sum() <= 1e-6
+
+
+def test_symmetric_unequal_masses_and_scaling():
+    """Lognormal masses exercise the -m_i/m_j weighting of the second body's
+    share; power-of-two G and mass scaling stay bitwise."""
+    pm, _ = workloads.uniform_cube(7000, seed=12, masses="lognormal")
+    a = sym_accel(pm, eps2=1e-6)
+    assert_parity(a, ref_accel(pm, eps2=1e-6), "symmetric lognormal 7000")
+    assert np.array_equal(sym_accel(pm, G=2.0, eps2=1e-6), 2 * a)
+    pm2 = pm.copy()
+    pm2[:, 3] *= 4
+    assert np.array_equal(sym_accel(pm2, eps2=1e-6), 4 * a)
+
+
+def test_symmetric_plummer1m_sampled():
+    w = workloads.WORKLOADS["plummer1m"]
+    pm, _ = workloads.make("plummer1m")
+    rows = sample_rows(w.n, 384, seed=7)
+    log("symmetric plummer1m: oracle rows")
+    ref = ref_accel(pm, w.G, w.eps2, rows)
+    a = sym_accel(pm, w.G, w.eps2)
+    assert np.all(a[:, 3] == 0)
+    assert_parity(a[rows], ref, "symmetric plummer1m")
+    # the one-sided pass agrees over all bodies (different summation order)
+    assert_parity(a, gpu_accel(pm, w.G, w.eps2).astype(np.float64), "symmetric vs one-sided 1m")
+
+
+def test_symmetric_collision1m_ragged_sampled():
+    w = workloads.WORKLOADS["collision1m"]
+    pm, _ = workloads.make("collision1m")
+    rows = sample_rows(w.n, 256, seed=8)
+    ref = ref_accel(pm, w.G, w.eps2, rows)
+    a = sym_accel(pm, w.G, w.eps2)
+    assert_parity(a[rows], ref, "symmetric collision1m")
