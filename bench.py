@@ -128,6 +128,19 @@ def sweep(nb, torch, w, pm, acc, reps, paths):
         _sweep_line(w, ms, symmetric_variant=v, panel=nb.nbody_accel_symmetric_panel(v),
                     workspace_bytes=need)
         del ws
+    if "range" in paths:
+        # one GPU's share of an i-split over 8 GPUs: N/8 i-bodies against all N
+        ni = w.n // 8
+        out = torch.empty((ni, 4), dtype=torch.float32, device=pm.device)
+        for v in range(nb.nbody_accel_variant_count()):
+            ms = _time(torch, lambda: nb.nbody_accel_range(pm, 0, ni, w.G, w.eps2, out, v), reps)
+            best = min(ms)
+            inter = float(ni) * float(w.n)
+            tflops = FLOPS_PER_INTERACTION * inter / (best * 1e-3) / 1e12
+            print(json.dumps({"workload": w.name, "n": w.n, "share": [0, ni], "range_variant": v,
+                              "tiling": nb.nbody_accel_variant_info(v), "ms_min": best,
+                              "interactions_per_s_billions": inter / (best * 1e-3) / 1e9,
+                              "pct_fp32_peak": 100 * tflops / PEAK_FP32_TFLOPS}), flush=True)
     for j_chunk in SPLITJ_CHUNKS if "splitj" in paths else ():
         need = nb.nbody_accel_splitj_workspace_bytes(w.n, j_chunk)
         if need > SPLITJ_MAX_WORKSPACE or -(-w.n // j_chunk) > 65535:
@@ -156,7 +169,7 @@ def main():
                          "instead of the step benchmark")
     ap.add_argument("--reps", type=int, default=3, help="timed force passes per variant (--sweep)")
     ap.add_argument("--sweep-paths", default="tile,symmetric,splitj",
-                    help="comma-separated subset of tile, symmetric, splitj (--sweep)")
+                    help="comma-separated subset of tile, symmetric, splitj, range (--sweep)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

@@ -33,6 +33,8 @@ EXPORTS = (
     "nbody_status_string", "nbody_abi_version",
     "nbody_accel", "nbody_accel_variant", "nbody_accel_variant_count",
     "nbody_accel_variant_info", "nbody_accel_variant_for_n",
+    "nbody_accel_range", "nbody_accel_potential",
+    "nbody_energy_from_potential", "nbody_energy_from_potential_workspace_bytes",
     "nbody_accel_splitj", "nbody_accel_splitj_workspace_bytes",
     "nbody_accel_symmetric", "nbody_accel_symmetric_workspace_bytes",
     "nbody_accel_symmetric_variant_count", "nbody_accel_symmetric_panel",
@@ -76,6 +78,10 @@ def load_library(path: str | None = None):
         "nbody_accel_variant_count": (c_int, []),
         "nbody_accel_variant_info": (c_int, [c_int, pint, pint, pint, pint]),
         "nbody_accel_variant_for_n": (c_int, [c_i64]),
+        "nbody_accel_potential": (c_int, [vp, c_i64, c_f, c_f, vp, vp]),
+        "nbody_energy_from_potential": (c_int, [vp, vp, vp, c_i64, vp, c_sz, vp, vp]),
+        "nbody_energy_from_potential_workspace_bytes": (c_sz, [c_i64]),
+        "nbody_accel_range": (c_int, [vp, c_i64, c_i64, c_i64, c_f, c_f, vp, c_int, vp]),
         "nbody_accel_splitj": (c_int, [vp, c_i64, c_f, c_f, vp, c_i64, vp, c_sz, vp]),
         "nbody_accel_splitj_workspace_bytes": (c_sz, [c_i64, c_i64]),
         "nbody_accel_symmetric": (c_int, [vp, c_i64, c_f, c_f, vp, c_int, vp, c_sz, vp]),
@@ -187,6 +193,48 @@ def nbody_accel_variant_info(v: int) -> dict:
 
 def nbody_accel_variant_for_n(n: int) -> int:
     return int(load_library().nbody_accel_variant_for_n(int(n)))
+
+
+def nbody_accel_potential(posmass, G: float, eps2: float, accel_out, stream=None):
+    """accel_out[i] = (a_i, Phi_i) with Phi_i the softened potential at body i."""
+    n = _n_of(posmass)
+    if _n_of(accel_out) != n:
+        raise ValueError("accel_out must have N rows")
+    _check(load_library().nbody_accel_potential(_f32(posmass, "posmass", (4,)), n, G, eps2,
+                                                _f32(accel_out, "accel_out", (4,)),
+                                                _stream(stream)),
+           "nbody_accel_potential")
+
+
+def nbody_energy_from_potential_workspace_bytes(n: int) -> int:
+    return int(load_library().nbody_energy_from_potential_workspace_bytes(int(n)))
+
+
+def nbody_energy_from_potential(posmass, vel, accel_pot, workspace, stats_out, stream=None):
+    torch = _torch()
+    n = _n_of(posmass)
+    if _n_of(vel) != n or _n_of(accel_pot) != n:
+        raise ValueError("posmass, vel and accel_pot must have N rows")
+    if stats_out.numel() < 8:
+        raise ValueError("stats_out needs 8 doubles")
+    ws = _dev(workspace, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load_library().nbody_energy_from_potential(
+        _f32(posmass, "posmass", (4,)), _f32(vel, "vel", (4,)), _f32(accel_pot, "accel_pot", (4,)),
+        n, ws, nbytes, _dev(stats_out, "stats_out", None, torch.float64), _stream(stream)),
+        "nbody_energy_from_potential")
+
+
+def nbody_accel_range(posmass, i0: int, ni: int, G: float, eps2: float, accel_out,
+                      variant: int = -1, stream=None):
+    """accel_out[r] = (a_{i0+r}, 0) for r < ni, summed over all N bodies."""
+    n = _n_of(posmass)
+    if _n_of(accel_out) != ni:
+        raise ValueError("accel_out must have ni rows")
+    _check(load_library().nbody_accel_range(_f32(posmass, "posmass", (4,)), n, int(i0), int(ni),
+                                            G, eps2, _f32(accel_out, "accel_out", (4,)),
+                                            int(variant), _stream(stream)),
+           "nbody_accel_range")
 
 
 def nbody_accel_splitj_workspace_bytes(n: int, j_chunk: int) -> int:

@@ -46,7 +46,7 @@ int force_aos4(const float *posmass, int64_t n, float G, float eps2, float *acce
   BodyArrays b;
   b.posmass = posmass;
   b.accel4 = accel_out;
-  return hip_status(nbody::launch_force(variant, Layout::Aos4, b, (int)n, G, eps2,
+  return hip_status(nbody::launch_force(variant, Layout::Aos4, b, (int)n, 0, (int)n, G, eps2,
                                         as_stream(stream)));
 }
 
@@ -101,6 +101,36 @@ int nbody_accel_variant(const float *posmass, int64_t n, float G, float eps2, fl
   return force_aos4(posmass, n, G, eps2, accel_out, variant, stream);
 }
 
+int nbody_accel_potential(const float *posmass, int64_t n, float G, float eps2,
+                          float *accel_out, void *stream) {
+  if (!n_ok(n)) return NBODY_ERR_INVALID_ARG;
+  if (int s = check_consts(G, eps2)) return s;
+  if (n == 0) return NBODY_OK;
+  if (!posmass || !accel_out) return NBODY_ERR_INVALID_ARG;
+  if (!aligned(posmass, 16) || !aligned(accel_out, 16)) return NBODY_ERR_ALIGNMENT;
+  const size_t bytes = (size_t)n * 16;
+  if (overlap(posmass, bytes, accel_out, bytes)) return NBODY_ERR_ALIAS;
+  return hip_status(
+      nbody::launch_force_potential(posmass, (int)n, G, eps2, accel_out, as_stream(stream)));
+}
+
+int nbody_accel_range(const float *posmass, int64_t n, int64_t i0, int64_t ni, float G,
+                      float eps2, float *accel_out, int variant, void *stream) {
+  if (!n_ok(n) || i0 < 0 || ni < 0 || i0 > n || ni > n - i0) return NBODY_ERR_INVALID_ARG;
+  if (int s = check_consts(G, eps2)) return s;
+  const int v = variant < 0 ? nbody::force_variant_for_n(ni) : variant;
+  if (!nbody::force_variant(v)) return NBODY_ERR_INVALID_ARG;
+  if (ni == 0) return NBODY_OK;
+  if (!posmass || !accel_out) return NBODY_ERR_INVALID_ARG;
+  if (!aligned(posmass, 16) || !aligned(accel_out, 16)) return NBODY_ERR_ALIGNMENT;
+  if (overlap(posmass, (size_t)n * 16, accel_out, (size_t)ni * 16)) return NBODY_ERR_ALIAS;
+  BodyArrays b;
+  b.posmass = posmass;
+  b.accel4 = accel_out;
+  return hip_status(nbody::launch_force(v, Layout::Aos4, b, (int)n, (int)i0, (int)ni, G, eps2,
+                                        as_stream(stream)));
+}
+
 int nbody_accel_f3aos(const float *pos, const float *mass, int64_t n, float G, float eps2,
                       float *accel_out, void *stream) {
   if (!n_ok(n)) return NBODY_ERR_INVALID_ARG;
@@ -115,7 +145,7 @@ int nbody_accel_f3aos(const float *pos, const float *mass, int64_t n, float G, f
   b.mass = mass;
   b.accel3 = accel_out;
   return hip_status(nbody::launch_force(nbody::force_variant_for_n(n), Layout::Aos3, b, (int)n,
-                                        G, eps2, as_stream(stream)));
+                                        0, (int)n, G, eps2, as_stream(stream)));
 }
 
 int nbody_accel_soa(const float *x, const float *y, const float *z, const float *m, int64_t n,
@@ -148,8 +178,8 @@ int nbody_accel_soa(const float *x, const float *y, const float *z, const float 
   b.ax = ax;
   b.ay = ay;
   b.az = az;
-  return hip_status(nbody::launch_force(nbody::force_variant_for_n(n), Layout::Soa, b, (int)n, G,
-                                        eps2, as_stream(stream)));
+  return hip_status(nbody::launch_force(nbody::force_variant_for_n(n), Layout::Soa, b, (int)n, 0,
+                                        (int)n, G, eps2, as_stream(stream)));
 }
 
 size_t nbody_accel_splitj_workspace_bytes(int64_t n, int64_t j_chunk) {
@@ -242,6 +272,33 @@ int nbody_kick(float *vel, const float *accel, float h, int64_t n, void *stream)
   const size_t bytes = (size_t)n * 16;
   if (overlap(vel, bytes, accel, bytes)) return NBODY_ERR_ALIAS;
   return hip_status(nbody::launch_kick(vel, accel, h, (int)n, as_stream(stream)));
+}
+
+size_t nbody_energy_from_potential_workspace_bytes(int64_t n) {
+  if (!n_ok(n)) return 0;
+  return nbody::energy_from_potential_workspace_bytes(n);
+}
+
+int nbody_energy_from_potential(const float *posmass, const float *vel, const float *accel_pot,
+                                int64_t n, void *workspace, size_t workspace_bytes,
+                                double *stats_out, void *stream) {
+  if (!n_ok(n)) return NBODY_ERR_INVALID_ARG;
+  if (n == 0) return NBODY_OK;
+  if (!posmass || !vel || !accel_pot || !stats_out) return NBODY_ERR_INVALID_ARG;
+  if (!aligned(posmass, 16) || !aligned(vel, 16) || !aligned(accel_pot, 16) ||
+      !aligned(stats_out, 8))
+    return NBODY_ERR_ALIGNMENT;
+  const size_t need = nbody::energy_from_potential_workspace_bytes(n);
+  if (!workspace || workspace_bytes < need) return NBODY_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return NBODY_ERR_ALIGNMENT;
+  const size_t bytes = (size_t)n * 16, sb = 8 * sizeof(double);
+  const void *in[3] = {posmass, vel, accel_pot};
+  for (const void *p : in)
+    if (overlap(workspace, need, p, bytes) || overlap(stats_out, sb, p, bytes))
+      return NBODY_ERR_ALIAS;
+  if (overlap(workspace, need, stats_out, sb)) return NBODY_ERR_ALIAS;
+  return hip_status(nbody::launch_energy_from_potential(posmass, vel, accel_pot, (int)n, workspace,
+                                                        stats_out, as_stream(stream)));
 }
 
 size_t nbody_energy_workspace_bytes(int64_t n) {

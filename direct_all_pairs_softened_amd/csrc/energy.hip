@@ -159,6 +159,42 @@ __global__ __launch_bounds__(kFinalThreads) void energy_final_kernel(
   }
 }
 
+// O(N) energy from per-body potentials Phi_i (accel.w of the potential
+// force pass): K_i = m v^2 / 2, W_i = m_i Phi_i / 2, P, M; fp64 tree per
+// block, then energy_final_kernel.
+constexpr int kFromPotThreads = 256;
+
+__global__ __launch_bounds__(kFromPotThreads) void energy_from_potential_kernel(
+    const float4 *__restrict__ pm, const float4 *__restrict__ vel,
+    const float4 *__restrict__ acc, int n, double *__restrict__ block_out) {
+  __shared__ double red[kEnergyFields][kFromPotThreads];
+  const int tid = threadIdx.x;
+  const int i = blockIdx.x * kFromPotThreads + tid;
+  double f[kEnergyFields] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+  if (i < n) {
+    const float4 b = pm[i], v = vel[i], a = acc[i];
+    const double m = (double)b.w;
+    const double vx = v.x, vy = v.y, vz = v.z;
+    f[0] = 0.5 * m * (vx * vx + vy * vy + vz * vz);
+    f[1] = 0.5 * m * (double)a.w;
+    f[2] = m * vx;
+    f[3] = m * vy;
+    f[4] = m * vz;
+    f[5] = m;
+  }
+#pragma unroll
+  for (int c = 0; c < kEnergyFields; ++c) red[c][tid] = f[c];
+  __syncthreads();
+  for (int s = kFromPotThreads / 2; s > 0; s >>= 1) {
+    if (tid < s) {
+#pragma unroll
+      for (int c = 0; c < kEnergyFields; ++c) red[c][tid] += red[c][tid + s];
+    }
+    __syncthreads();
+  }
+  if (tid < kEnergyFields) block_out[(size_t)blockIdx.x * 8 + tid] = red[tid][0];
+}
+
 struct EnergyShape {
   int T, waves, split;
 };
@@ -187,6 +223,27 @@ hipError_t launch_partial(const float4 *pm, const float4 *vel, int n, float G, f
 }
 
 }  // namespace
+
+size_t energy_from_potential_workspace_bytes(int64_t n) {
+  if (n <= 0) return 0;
+  return (size_t)((n + kFromPotThreads - 1) / kFromPotThreads) * 8 * sizeof(double);
+}
+
+hipError_t launch_energy_from_potential(const float *posmass, const float *vel,
+                                        const float *accel, int n, void *workspace,
+                                        double *stats, hipStream_t stream) {
+  const int blocks = (n + kFromPotThreads - 1) / kFromPotThreads;
+  double *block_out = reinterpret_cast<double *>(workspace);
+  hipLaunchKernelGGL(energy_from_potential_kernel, dim3(blocks), dim3(kFromPotThreads), 0, stream,
+                     reinterpret_cast<const float4 *>(posmass),
+                     reinterpret_cast<const float4 *>(vel), reinterpret_cast<const float4 *>(accel),
+                     n, block_out);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(energy_final_kernel, dim3(1), dim3(kFinalThreads), 0, stream, block_out,
+                     blocks, stats);
+  return hipGetLastError();
+}
 
 size_t energy_workspace_bytes(int64_t n) {
   if (n <= 0) return 0;

@@ -14,6 +14,8 @@
 //  - tiles are double-buffered: the next tile's global loads are issued
 //    before the current tile's arithmetic and written to the other LDS buffer
 //    after it, so there is one barrier per tile;
+//  - the i side may be a sub-range [i0, i0 + ni) of the bodies (one GPU's
+//    share when the pass is split by i); output row r is body i0 + r;
 //  - ragged n: staged indices are clamped into [0, n) and the mass of every
 //    padding slot is zeroed, so the inner loop has no bounds test and a
 //    padding term adds exactly +0 (README section 3.1 guards the same tail
@@ -27,10 +29,15 @@ namespace nbody {
 
 // OCC > 0 asks the compiler to fit OCC waves per SIMD (it then caps VGPRs at
 // 512 / OCC); 0 leaves the register budget to the compiler.
-template <int K, int T, int WAVES, int S, int U, int OCC, class L>
+//
+// POT = true also sums phi_i = sum_{j != i} m_j (r^2 + eps^2)^{-1/2}
+// (two-level like the acceleration; the j = i pair is dropped by an index
+// test, three more VALU ops per pair) and stores Phi_i = -G phi_i in the
+// output's w.
+template <int K, int T, int WAVES, int S, int U, int OCC, class L, bool POT = false>
 __global__ __launch_bounds__(WAVES *kWave)
 __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1))) void force_tile_kernel(
-    L lay, int n, int n_tiles, int tiles_per_part, float G, float eps2) {
+    L lay, int n, int i0, int ni, int n_tiles, int tiles_per_part, float G, float eps2) {
   constexpr int GW = WAVES / S;            // i-groups (waves) per part
   constexpr int NTHREADS = WAVES * kWave;  // threads per block
   constexpr int LOADS = (S * T) / NTHREADS;
@@ -47,17 +54,18 @@ __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1))) void force_tile_kernel(
   const int grp = wave % GW;
   const int base = blockIdx.x * (GW * kWave * K) + grp * kWave + lane;
 
-  float xi[K], yi[K], zi[K], ax[K], ay[K], az[K];
+  float xi[K], yi[K], zi[K], ax[K], ay[K], az[K], ap[K];
 #pragma unroll
   for (int q = 0; q < K; ++q) {
     const int i = base + q * GW * kWave;
-    const float4 b = lay.load(i < n ? i : n - 1);
+    const float4 b = lay.load(i0 + (i < ni ? i : ni - 1));
     xi[q] = b.x;
     yi[q] = b.y;
     zi[q] = b.z;
     ax[q] = 0.0f;
     ay[q] = 0.0f;
     az[q] = 0.0f;
+    ap[q] = 0.0f;
   }
 
   // Staging slot e of a step holds body jj = e % T of part e / T's tile.
@@ -92,25 +100,35 @@ __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1))) void force_tile_kernel(
     if (more) fetch(step + 1);
     if (part * tiles_per_part + step < n_tiles) {
       const float4 *tp = &tile[cur][part * T];
-      float px[K], py[K], pz[K];
+      const int j0 = (part * tiles_per_part + step) * T;
+      float px[K], py[K], pz[K], pp[K];
 #pragma unroll
       for (int q = 0; q < K; ++q) {
         px[q] = 0.0f;
         py[q] = 0.0f;
         pz[q] = 0.0f;
+        pp[q] = 0.0f;
       }
 #pragma unroll U
       for (int jj = 0; jj < T; ++jj) {
         const float4 b = tp[jj];
 #pragma unroll
-        for (int q = 0; q < K; ++q)
-          pair_accel(b.x, b.y, b.z, b.w, xi[q], yi[q], zi[q], eps2, px[q], py[q], pz[q]);
+        for (int q = 0; q < K; ++q) {
+          if constexpr (POT) {
+            const float mp = (j0 + jj == i0 + base + q * GW * kWave) ? 0.0f : b.w;
+            pair_accel_pot(b.x, b.y, b.z, b.w, mp, xi[q], yi[q], zi[q], eps2, px[q], py[q],
+                           pz[q], pp[q]);
+          }
+          else
+            pair_accel(b.x, b.y, b.z, b.w, xi[q], yi[q], zi[q], eps2, px[q], py[q], pz[q]);
+        }
       }
 #pragma unroll
       for (int q = 0; q < K; ++q) {
         ax[q] += px[q];
         ay[q] += py[q];
         az[q] += pz[q];
+        if constexpr (POT) ap[q] += pp[q];
       }
     }
     if (more) stash(cur ^ 1);
@@ -141,6 +159,18 @@ __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1))) void force_tile_kernel(
           az[q] += red[o + 2 * kWave];
         }
       }
+      if constexpr (POT) {
+        __syncthreads();
+        if (part == p) {
+#pragma unroll
+          for (int q = 0; q < K; ++q) red[(grp * K + q) * kWave + lane] = ap[q];
+        }
+        __syncthreads();
+        if (part == 0) {
+#pragma unroll
+          for (int q = 0; q < K; ++q) ap[q] += red[(grp * K + q) * kWave + lane];
+        }
+      }
     }
   }
 
@@ -148,20 +178,26 @@ __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1))) void force_tile_kernel(
 #pragma unroll
     for (int q = 0; q < K; ++q) {
       const int i = base + q * GW * kWave;
-      if (i < n) lay.store(i, G * ax[q], G * ay[q], G * az[q]);
+      if constexpr (POT) {
+        if (i < ni) lay.store4(i, G * ax[q], G * ay[q], G * az[q], -G * ap[q]);
+      } else {
+        if (i < ni) lay.store(i, G * ax[q], G * ay[q], G * az[q]);
+      }
     }
   }
 }
 
-template <int K, int T, int WAVES, int S, int U, int OCC, class L>
-static hipError_t launch_tile(const L &lay, int n, float G, float eps2, hipStream_t stream) {
+template <int K, int T, int WAVES, int S, int U, int OCC, class L, bool POT = false>
+static hipError_t launch_tile(const L &lay, int n, int i0, int ni, float G, float eps2,
+                              hipStream_t stream) {
   constexpr int GW = WAVES / S;
   const int per_block = GW * kWave * K;
-  const int blocks = (n + per_block - 1) / per_block;
+  const int blocks = (ni + per_block - 1) / per_block;
   const int n_tiles = (n + T - 1) / T;
   const int tiles_per_part = (n_tiles + S - 1) / S;
-  hipLaunchKernelGGL((force_tile_kernel<K, T, WAVES, S, U, OCC, L>), dim3(blocks),
-                     dim3(WAVES * kWave), 0, stream, lay, n, n_tiles, tiles_per_part, G, eps2);
+  hipLaunchKernelGGL((force_tile_kernel<K, T, WAVES, S, U, OCC, L, POT>), dim3(blocks),
+                     dim3(WAVES * kWave), 0, stream, lay, n, i0, ni, n_tiles, tiles_per_part, G,
+                     eps2);
   return hipGetLastError();
 }
 
@@ -213,11 +249,12 @@ int force_variant_for_n(int64_t n) {
 }
 
 template <class L>
-static hipError_t dispatch(int v, const L &lay, int n, float G, float eps2, hipStream_t stream) {
+static hipError_t dispatch(int v, const L &lay, int n, int i0, int ni, float G, float eps2,
+                           hipStream_t stream) {
   switch (v) {
 #define X(id, K, T, W, S, U, OCC) \
   case id:                        \
-    return launch_tile<K, T, W, S, U, OCC>(lay, n, G, eps2, stream);
+    return launch_tile<K, T, W, S, U, OCC>(lay, n, i0, ni, G, eps2, stream);
     NBODY_FORCE_VARIANTS(X)
 #undef X
     default:
@@ -225,21 +262,41 @@ static hipError_t dispatch(int v, const L &lay, int n, float G, float eps2, hipS
   }
 }
 
-hipError_t launch_force(int variant, Layout layout, const BodyArrays &b, int n, float G,
-                        float eps2, hipStream_t stream) {
+// Variants compiled with the potential sum (the ones force_variant_for_n
+// picks).
+#define NBODY_POT_VARIANTS(X) \
+  X(11, 1, 64, 16, 16, 4, 0)  \
+  X(16, 2, 256, 8, 2, 4, 8)
+
+hipError_t launch_force_potential(const float *posmass, int n, float G, float eps2,
+                                  float *accel, hipStream_t stream) {
+  LayoutAos4 lay{reinterpret_cast<const float4 *>(posmass), reinterpret_cast<float4 *>(accel)};
+  switch (force_variant_for_n(n)) {
+#define X(id, K, T, W, S, U, OCC) \
+  case id:                        \
+    return launch_tile<K, T, W, S, U, OCC, LayoutAos4, true>(lay, n, 0, n, G, eps2, stream);
+    NBODY_POT_VARIANTS(X)
+#undef X
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_force(int variant, Layout layout, const BodyArrays &b, int n, int i0, int ni,
+                        float G, float eps2, hipStream_t stream) {
   switch (layout) {
     case Layout::Aos4: {
       LayoutAos4 lay{reinterpret_cast<const float4 *>(b.posmass),
                      reinterpret_cast<float4 *>(b.accel4)};
-      return dispatch(variant, lay, n, G, eps2, stream);
+      return dispatch(variant, lay, n, i0, ni, G, eps2, stream);
     }
     case Layout::Aos3: {
       LayoutAos3 lay{b.pos3, b.mass, b.accel3};
-      return dispatch(variant, lay, n, G, eps2, stream);
+      return dispatch(variant, lay, n, i0, ni, G, eps2, stream);
     }
     case Layout::Soa: {
       LayoutSoa lay{b.x, b.y, b.z, b.m, b.ax, b.ay, b.az};
-      return dispatch(variant, lay, n, G, eps2, stream);
+      return dispatch(variant, lay, n, i0, ni, G, eps2, stream);
     }
   }
   return hipErrorInvalidValue;

@@ -37,6 +37,29 @@ __device__ __forceinline__ void pair_accel(float xj, float yj, float zj, float m
   pz = __builtin_fmaf(s, dz, pz);
 }
 
+// pair_accel plus the potential sum p += mp (|r|^2 + eps^2)^{-1/2}, where the
+// caller passes mp = m_j, or 0 for the j = i pair (the self term m_i / eps is
+// excluded exactly: summing it and subtracting it later would cancel away
+// digits whenever m_i / eps dwarfs the potential).  The acceleration
+// arithmetic is the same instruction sequence as pair_accel, so (px, py, pz)
+// come out bitwise equal to it.
+__device__ __forceinline__ void pair_accel_pot(float xj, float yj, float zj, float mj, float mp,
+                                               float xi, float yi, float zi, float eps2,
+                                               float &px, float &py, float &pz, float &pp) {
+  const float dx = xj - xi;
+  const float dy = yj - yi;
+  const float dz = zj - zi;
+  float d2 = __builtin_fmaf(dx, dx, eps2);
+  d2 = __builtin_fmaf(dy, dy, d2);
+  d2 = __builtin_fmaf(dz, dz, d2);
+  const float inv = __builtin_amdgcn_rsqf(d2);
+  const float s = (mj * inv) * (inv * inv);
+  px = __builtin_fmaf(s, dx, px);
+  py = __builtin_fmaf(s, dy, py);
+  pz = __builtin_fmaf(s, dz, pz);
+  pp = __builtin_fmaf(mp, inv, pp);
+}
+
 // (|r|^2 + eps^2)^{-1/2} for one pair: the potential term of the energy is
 // m_j times this, with the j = i term dropped by the caller's index test.
 __device__ __forceinline__ float pair_rsq(float xj, float yj, float zj, float xi, float yi,
@@ -60,6 +83,9 @@ struct LayoutAos4 {
   __device__ __forceinline__ float4 load(int j) const { return pm[j]; }
   __device__ __forceinline__ void store(int i, float ax, float ay, float az) const {
     out[i] = make_float4(ax, ay, az, 0.0f);
+  }
+  __device__ __forceinline__ void store4(int i, float ax, float ay, float az, float w) const {
+    out[i] = make_float4(ax, ay, az, w);
   }
 };
 

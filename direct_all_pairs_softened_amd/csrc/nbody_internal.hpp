@@ -40,8 +40,14 @@ struct BodyArrays {
   float *ax = nullptr, *ay = nullptr, *az = nullptr;
 };
 
-hipError_t launch_force(int variant, Layout layout, const BodyArrays &b, int n, float G,
-                        float eps2, hipStream_t stream);
+// i side: bodies [i0, i0 + ni); output row r belongs to body i0 + r.
+hipError_t launch_force(int variant, Layout layout, const BodyArrays &b, int n, int i0, int ni,
+                        float G, float eps2, hipStream_t stream);
+
+// One-sided pass that also stores Phi_i = -G sum_{j != i} m_j / sqrt(r^2 + eps^2)
+// in accel.w (variant chosen by n).
+hipError_t launch_force_potential(const float *posmass, int n, float G, float eps2,
+                                  float *accel, hipStream_t stream);
 
 // Two-pass decomposition over j chunks.
 size_t splitj_workspace_bytes(int64_t n, int64_t j_chunk);
@@ -64,6 +70,10 @@ hipError_t launch_kick(float *vel, const float *accel, float h, int n, hipStream
 
 // Energy.
 size_t energy_workspace_bytes(int64_t n);
+size_t energy_from_potential_workspace_bytes(int64_t n);
+hipError_t launch_energy_from_potential(const float *posmass, const float *vel,
+                                        const float *accel, int n, void *workspace,
+                                        double *stats, hipStream_t stream);
 hipError_t launch_energy(const float *posmass, const float *vel, int n, float G, float eps2,
                          void *workspace, double *stats, hipStream_t stream);
 

@@ -110,6 +110,30 @@ int nbody_accel_variant_info(int v, int *bodies_per_lane, int *tile,
 /* The variant nbody_accel uses for n bodies. */
 int nbody_accel_variant_for_n(int64_t n);
 
+/* nbody_accel plus each body's softened potential in the output's w:
+ *   accel_out[i] = (ax, ay, az, Phi_i),
+ *   Phi_i = -G sum_{j != i} m_j / sqrt(|x_j - x_i|^2 + eps^2).
+ * The CAL IL loop of "CAL programming (4)" carries the same sum in the w
+ * lane of its accumulator (its rsq result times m_j).  The j = i pair is
+ * dropped from this sum by an index test.  The xyz outputs are bitwise equal
+ * to nbody_accel's for the same n.  About three more VALU ops per pair. */
+int nbody_accel_potential(const float *posmass, int64_t n, float G, float eps2,
+                          float *accel_out, void *stream);
+
+/* Accelerations of bodies [i0, i0 + ni) from all n bodies: the one-sided
+ * pass restricted to a contiguous share of the i side, which is what one GPU
+ * computes when the pass is split by i ("Cuda Nbody Notes" splits the n
+ * bodies into independent blocks of p the same way).
+ *   0 <= i0, 0 <= ni, i0 + ni <= n; ni == 0 is a no-op.
+ *   accel_out  [ni] float4: row r receives body i0 + r.  Must not overlap
+ *              posmass.
+ *   variant    a compiled variant, or -1 for nbody_accel_variant_for_n(ni).
+ * With the same variant, row r is bitwise equal to row i0 + r of
+ * nbody_accel_variant(..., variant): the j side and its order are the same. */
+int nbody_accel_range(const float *posmass, int64_t n, int64_t i0, int64_t ni,
+                      float G, float eps2, float *accel_out, int variant,
+                      void *stream);
+
 /* Two-pass ("2D") decomposition: the j range is cut into chunks of j_chunk
  * bodies (j_chunk a multiple of 32, >= 32); a first kernel writes one
  * float4 partial per (chunk, body) into the workspace, a second adds the
@@ -207,6 +231,18 @@ int nbody_energy(const float *posmass, const float *vel, int64_t n, float G,
                  double *stats_out, void *stream);
 
 size_t nbody_energy_workspace_bytes(int64_t n);
+
+/* Energy and momentum in O(n) from the potentials nbody_accel_potential
+ * stored in accel_pot[i].w: stats_out = {K, W, K + W, Px, Py, Pz, M, 0}
+ * with W = sum_i m_i Phi_i / 2 (each pair once).  fp64 fixed-order
+ * reduction as in nbody_energy.
+ *   workspace  >= nbody_energy_from_potential_workspace_bytes(n) bytes,
+ *              16-byte aligned, disjoint from every other argument. */
+int nbody_energy_from_potential(const float *posmass, const float *vel,
+                                const float *accel_pot, int64_t n,
+                                void *workspace, size_t workspace_bytes,
+                                double *stats_out, void *stream);
+size_t nbody_energy_from_potential_workspace_bytes(int64_t n);
 
 #ifdef __cplusplus
 }

@@ -193,3 +193,37 @@ def test_symmetric_host_side(lib):
     assert f(vp(A), 1000, 1.0, 1e-4, vp(B), 0, vp(B - 64), need, None) == nb.NBODY_ERR_ALIAS
     # more panel pairs than a grid holds
     assert f(vp(A), nb.NBODY_MAX_N, 1.0, 1e-4, vp(B), 0, vp(C), 1 << 62, None) == nb.NBODY_ERR_INVALID_ARG
+
+
+def test_range_validation(lib):
+    f = lib.nbody_accel_range
+    assert f(vp(A), 100, 0, 0, 1.0, 1e-4, vp(B), -1, None) == nb.NBODY_OK          # empty share
+    assert f(vp(A), 100, 100, 0, 1.0, 1e-4, vp(B), -1, None) == nb.NBODY_OK
+    assert f(vp(A), 100, -1, 10, 1.0, 1e-4, vp(B), -1, None) == nb.NBODY_ERR_INVALID_ARG
+    assert f(vp(A), 100, 0, -1, 1.0, 1e-4, vp(B), -1, None) == nb.NBODY_ERR_INVALID_ARG
+    assert f(vp(A), 100, 95, 6, 1.0, 1e-4, vp(B), -1, None) == nb.NBODY_ERR_INVALID_ARG
+    assert f(vp(A), 100, 101, 0, 1.0, 1e-4, vp(B), -1, None) == nb.NBODY_ERR_INVALID_ARG
+    assert f(vp(A), 100, 0, 10, 1.0, 1e-4, vp(B), 10 ** 6, None) == nb.NBODY_ERR_INVALID_ARG
+    assert f(vp(A), 100, 0, 10, 1.0, 0.0, vp(B), -1, None) == nb.NBODY_ERR_INVALID_ARG
+    assert f(vp(A), 100, 0, 10, 1.0, 1e-4, None, -1, None) == nb.NBODY_ERR_INVALID_ARG
+    assert f(vp(A), 100, 0, 10, 1.0, 1e-4, vp(B + 4), -1, None) == nb.NBODY_ERR_ALIGNMENT
+    # the output may not overlap any of the n input rows, even outside the share
+    assert f(vp(A), 100, 0, 10, 1.0, 1e-4, vp(A + 16 * 50), -1, None) == nb.NBODY_ERR_ALIAS
+    assert f(vp(A), 100, 0, 10, 1.0, 1e-4, vp(A - 16 * 5), -1, None) == nb.NBODY_ERR_ALIAS
+
+
+def test_potential_and_energy_from_potential_validation(lib):
+    f = lib.nbody_accel_potential
+    assert f(vp(A), 0, 1.0, 1e-4, vp(B), None) == nb.NBODY_OK
+    assert f(vp(A), 10, 1.0, 0.0, vp(B), None) == nb.NBODY_ERR_INVALID_ARG
+    assert f(vp(A), 10, 1.0, 1e-4, vp(A), None) == nb.NBODY_ERR_ALIAS
+    assert f(vp(A + 8), 10, 1.0, 1e-4, vp(B), None) == nb.NBODY_ERR_ALIGNMENT
+    e = lib.nbody_energy_from_potential
+    need = nb.nbody_energy_from_potential_workspace_bytes(1000)
+    assert need == 4 * 8 * 8
+    assert e(vp(A), vp(B), vp(C), 0, None, 0, None, None) == nb.NBODY_OK
+    assert e(vp(A), vp(B), None, 1000, vp(D), need, vp(D + need), None) == nb.NBODY_ERR_INVALID_ARG
+    assert e(vp(A), vp(B), vp(C), 1000, vp(D), need - 1, vp(D + need), None) == nb.NBODY_ERR_WORKSPACE
+    assert e(vp(A), vp(B), vp(C), 1000, vp(D), need, vp(D + need + 4), None) == nb.NBODY_ERR_ALIGNMENT
+    assert e(vp(A), vp(B), vp(C), 1000, vp(C + 16), need, vp(D), None) == nb.NBODY_ERR_ALIAS
+    assert e(vp(A), vp(B), vp(C), 1000, vp(D), need, vp(D + 8), None) == nb.NBODY_ERR_ALIAS

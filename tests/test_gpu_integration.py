@@ -186,3 +186,64 @@ def test_collision1m_twenty_steps():
     ref = oracle.accel_rows(pos, mass, w.G, float(F32(w.eps2)), rows)
     assert_parity(acc.cpu().numpy()[rows], ref, "collision1m step 20")
     assert np.array_equal(pm_np[:, 3], pm0[:, 3])
+
+
+# ---------------------------------------------------------------------------
+# Potential carried in accel.w, and the O(N) energy built from it
+# ---------------------------------------------------------------------------
+
+def gpu_potential(pm_np, G=1.0, eps2=1e-4):
+    t = to_dev(pm_np)
+    out = torch.full_like(t, float("nan"))
+    nb.nbody_accel_potential(t, G, eps2, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 1000, 4097, 16384, 70000])
+def test_potential_pass(n):
+    """xyz bitwise equal to nbody_accel; w = Phi_i against the oracle."""
+    pm, _ = workloads.plummer(n, seed=30 + n) if n > 2 else workloads.uniform_cube(n, seed=n)
+    G, eps2 = 1.5, 1e-4
+    a = gpu_potential(pm, G, eps2)
+    t = to_dev(pm)
+    plain = torch.empty_like(t)
+    nb.nbody_accel(t, G, eps2, plain)
+    torch.cuda.synchronize()
+    assert np.array_equal(a[:, :3], plain.cpu().numpy()[:, :3])
+    if n == 1:
+        assert a[0, 3] == 0.0
+        return
+    pos, mass = oracle.split_posmass(pm)
+    rows = np.arange(n) if n <= 20000 else np.unique(np.concatenate(
+        [np.arange(64), np.arange(n - 64, n), np.random.default_rng(1).choice(n, 512, False)]))
+    ref = oracle.potential_rows(pos, mass, float(F32(G)), float(F32(eps2)), rows)
+    got = a[rows, 3].astype(np.float64)
+    l2 = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    worst = np.max(np.abs(got - ref) / np.abs(ref))
+    log(f"potential n={n}: rel L2 {l2:.2e}, worst {worst:.2e}")
+    assert l2 <= 1e-6 and worst <= 1e-5
+
+
+@pytest.mark.parametrize("name", ["uniform1k", "plummer16k"])
+def test_energy_from_potential(name):
+    w = workloads.WORKLOADS[name]
+    pm, vel = workloads.make(name)
+    a = to_dev(gpu_potential(pm, w.G, w.eps2))
+    ws = torch.empty(nb.nbody_energy_from_potential_workspace_bytes(w.n), dtype=torch.uint8,
+                     device=DEV)
+    stats = torch.zeros(8, dtype=torch.float64, device=DEV)
+    nb.nbody_energy_from_potential(to_dev(pm), to_dev(vel), a, ws, stats)
+    torch.cuda.synchronize()
+    e = dict(zip(nb.ENERGY_FIELDS, stats.cpu().tolist()))
+    r = ref_energy(pm, vel, w.G, w.eps2)
+    direct = gpu_energy(pm, vel, w.G, w.eps2)
+    assert abs(e["W"] - r["W"]) <= 2e-6 * abs(r["W"])
+    assert abs(e["W"] - direct["W"]) <= 2e-6 * abs(r["W"])
+    # same fp64 per-body terms as nbody_energy, summed by a different tree
+    mv = float((pm[:, 3].astype(np.float64) *
+                np.linalg.norm(vel[:, :3].astype(np.float64), axis=1)).sum())
+    assert abs(e["K"] - direct["K"]) <= 1e-13 * abs(direct["K"]) + 1e-300
+    assert abs(e["M"] - direct["M"]) <= 1e-13 * direct["M"]
+    for k in ("Px", "Py", "Pz"):
+        assert abs(e[k] - direct[k]) <= 1e-13 * mv, k

@@ -296,3 +296,36 @@ def test_symmetric_collision1m_ragged_sampled():
     ref = ref_accel(pm, w.G, w.eps2, rows)
     a = sym_accel(pm, w.G, w.eps2)
     assert_parity(a[rows], ref, "symmetric collision1m")
+
+
+# ---------------------------------------------------------------------------
+# One GPU's share of the i side
+# ---------------------------------------------------------------------------
+
+def range_accel(pm_np, i0, ni, G=1.0, eps2=1e-4, variant=-1):
+    t = torch.from_numpy(pm_np).to(DEV)
+    out = torch.full((ni, 4), float("nan"), device=DEV)
+    nb.nbody_accel_range(t, i0, ni, G, eps2, out, variant)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("variant", [2, 11, 16])
+def test_range_rows_bitwise_equal_full_pass(variant):
+    pm, _ = workloads.uniform_cube(5000, seed=21)
+    full = gpu_accel(pm, variant=variant)
+    for i0, ni in ((0, 5000), (0, 1), (17, 1000), (4999, 1), (1234, 2000), (3000, 2000)):
+        assert np.array_equal(range_accel(pm, i0, ni, variant=variant), full[i0:i0 + ni]), (i0, ni)
+    assert range_accel(pm, 10, 0).shape == (0, 4)
+
+
+def test_range_eighth_share_of_plummer1m():
+    """The shape one GPU of eight computes: 131072 i-bodies against all 2^20."""
+    w = workloads.WORKLOADS["plummer1m"]
+    pm, _ = workloads.make("plummer1m")
+    i0, ni = 3 * (w.n // 8), w.n // 8
+    a = range_accel(pm, i0, ni, w.G, w.eps2)
+    local = sample_rows(ni, 256, seed=9)
+    ref = ref_accel(pm, w.G, w.eps2, i0 + local)
+    assert np.all(a[:, 3] == 0)
+    assert_parity(a[local], ref, "1/8 share of plummer1m")
