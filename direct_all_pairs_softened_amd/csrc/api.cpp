@@ -79,13 +79,14 @@ int nbody_abi_version(void) { return NBODY_ABI_VERSION; }
 int nbody_accel_variant_count(void) { return nbody::force_variant_count(); }
 
 int nbody_accel_variant_info(int v, int *bodies_per_lane, int *tile, int *waves_per_block,
-                             int *split) {
+                             int *split, int *staging) {
   const nbody::ForceVariant *fv = nbody::force_variant(v);
   if (!fv) return NBODY_ERR_INVALID_ARG;
   if (bodies_per_lane) *bodies_per_lane = fv->bodies_per_lane;
   if (tile) *tile = fv->tile;
   if (waves_per_block) *waves_per_block = fv->waves;
   if (split) *split = fv->split;
+  if (staging) *staging = fv->staging;
   return NBODY_OK;
 }
 

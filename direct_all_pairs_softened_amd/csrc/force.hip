@@ -187,6 +187,76 @@ __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1))) void force_tile_kernel(
   }
 }
 
+// LDS-free variant (an ablation of the staging choice): each wave reads the
+// j-bodies straight from memory, in ascending j, with the same two-level sum
+// over chunks of T.  MODE 0 lets the compiler turn the wave-uniform loads into
+// scalar (SGPR) loads; MODE 1 forces vector loads of one address per wave
+// (the cache-only scheme the Handbook page mentions).  The j loop stops at
+// n (a wave-uniform bound), so there is no padding; with S = 1 and the same T
+// the sums are bitwise equal to the LDS kernel's.
+template <int K, int T, int WAVES, int MODE, int OCC>
+__global__ __launch_bounds__(WAVES *kWave)
+__attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1))) void force_stream_kernel(
+    const float4 *__restrict__ pm, int n, int i0, int ni, float G, float eps2,
+    float4 *__restrict__ out) {
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int base = blockIdx.x * (WAVES * kWave * K) + wave * kWave + lane;
+  int zero = 0;
+  if constexpr (MODE == 1) asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+  float xi[K], yi[K], zi[K], ax[K], ay[K], az[K];
+#pragma unroll
+  for (int q = 0; q < K; ++q) {
+    const int i = base + q * WAVES * kWave;
+    const float4 b = pm[i0 + (i < ni ? i : ni - 1)];
+    xi[q] = b.x;
+    yi[q] = b.y;
+    zi[q] = b.z;
+    ax[q] = 0.0f;
+    ay[q] = 0.0f;
+    az[q] = 0.0f;
+  }
+  for (int j0 = 0; j0 < n; j0 += T) {
+    const int cnt = min(T, n - j0);
+    float px[K], py[K], pz[K];
+#pragma unroll
+    for (int q = 0; q < K; ++q) {
+      px[q] = 0.0f;
+      py[q] = 0.0f;
+      pz[q] = 0.0f;
+    }
+#pragma unroll 4
+    for (int jj = 0; jj < cnt; ++jj) {
+      const float4 b = pm[j0 + jj + zero];
+#pragma unroll
+      for (int q = 0; q < K; ++q)
+        pair_accel(b.x, b.y, b.z, b.w, xi[q], yi[q], zi[q], eps2, px[q], py[q], pz[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < K; ++q) {
+      ax[q] += px[q];
+      ay[q] += py[q];
+      az[q] += pz[q];
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < K; ++q) {
+    const int i = base + q * WAVES * kWave;
+    if (i < ni) out[i] = make_float4(G * ax[q], G * ay[q], G * az[q], 0.0f);
+  }
+}
+
+template <int K, int T, int WAVES, int MODE, int OCC>
+static hipError_t launch_stream(const float *posmass, float *accel, int n, int i0, int ni,
+                                float G, float eps2, hipStream_t stream) {
+  const int per_block = WAVES * kWave * K;
+  const int blocks = (ni + per_block - 1) / per_block;
+  hipLaunchKernelGGL((force_stream_kernel<K, T, WAVES, MODE, OCC>), dim3(blocks),
+                     dim3(WAVES * kWave), 0, stream, reinterpret_cast<const float4 *>(posmass), n,
+                     i0, ni, G, eps2, reinterpret_cast<float4 *>(accel));
+  return hipGetLastError();
+}
+
 template <int K, int T, int WAVES, int S, int U, int OCC, class L, bool POT = false>
 static hipError_t launch_tile(const L &lay, int n, int i0, int ni, float G, float eps2,
                               hipStream_t stream) {
@@ -226,9 +296,20 @@ static hipError_t launch_tile(const L &lay, int n, int i0, int ni, float G, floa
   X(18, 4, 512, 8, 2, 2, 8)                                                    \
   X(19, 2, 512, 8, 1, 4, 8)      /* 1024 i per block, 1024 blocks x 8 waves */
 
+// LDS-free variants: (id, K, T, waves, mode, occupancy target); mode 0 =
+// scalar loads of j, 1 = vector loads of one address per wave.
+#define NBODY_STREAM_VARIANTS(X) \
+  X(20, 2, 256, 4, 0, 0)         \
+  X(21, 4, 256, 4, 0, 0)         \
+  X(22, 2, 256, 4, 1, 0)         \
+  X(23, 4, 256, 4, 1, 0)
+
 static const ForceVariant kVariants[] = {
-#define X(id, K, T, W, S, U, OCC) {K, T, W, S, U},
+#define X(id, K, T, W, S, U, OCC) {K, T, W, S, U, 0},
     NBODY_FORCE_VARIANTS(X)
+#undef X
+#define X(id, K, T, W, MODE, OCC) {K, T, W, 1, 4, 1 + MODE},
+        NBODY_STREAM_VARIANTS(X)
 #undef X
 };
 
@@ -284,6 +365,19 @@ hipError_t launch_force_potential(const float *posmass, int n, float G, float ep
 
 hipError_t launch_force(int variant, Layout layout, const BodyArrays &b, int n, int i0, int ni,
                         float G, float eps2, hipStream_t stream) {
+  const ForceVariant *fv = force_variant(variant);
+  if (fv && fv->staging != 0) {
+    if (layout != Layout::Aos4) return hipErrorInvalidValue;
+    switch (variant) {
+#define X(id, K, T, W, MODE, OCC) \
+  case id:                        \
+    return launch_stream<K, T, W, MODE, OCC>(b.posmass, b.accel4, n, i0, ni, G, eps2, stream);
+      NBODY_STREAM_VARIANTS(X)
+#undef X
+      default:
+        return hipErrorInvalidValue;
+    }
+  }
   switch (layout) {
     case Layout::Aos4: {
       LayoutAos4 lay{reinterpret_cast<const float4 *>(b.posmass),

@@ -19,6 +19,7 @@ struct ForceVariant {
   int waves;            // waves per block
   int split;            // S: j-parts per block (waves / S waves per part)
   int unroll;           // unroll of the inner j loop
+  int staging;          // 0: LDS tiles; 1: scalar loads of j; 2: vector loads of j
 };
 
 int force_variant_count();

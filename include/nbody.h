@@ -101,11 +101,16 @@ int nbody_accel_variant(const float *posmass, int64_t n, float G, float eps2,
 /* Number of compiled force variants. */
 int nbody_accel_variant_count(void);
 
-/* Describes variant v: bodies per lane, tile width T, waves per block, j
- * split S.  Returns NBODY_ERR_INVALID_ARG for an unknown v; any pointer
- * may be NULL to skip that field. */
+/* Describes variant v: bodies per lane, tile width T (the two-level
+ * summation chunk), waves per block, j split S, and how j-bodies reach the
+ * pair step (staging: 0 = LDS tiles read as wavefront broadcasts; 1 =
+ * wave-uniform scalar loads into SGPRs; 2 = vector loads of one address per
+ * wavefront, i.e. through the caches only).  Variants with staging != 0 are
+ * an ablation of the LDS design and exist for nbody_accel_variant and
+ * nbody_accel_range only.  Returns NBODY_ERR_INVALID_ARG for an unknown v;
+ * any pointer may be NULL to skip that field. */
 int nbody_accel_variant_info(int v, int *bodies_per_lane, int *tile,
-                             int *waves_per_block, int *split);
+                             int *waves_per_block, int *split, int *staging);
 
 /* The variant nbody_accel uses for n bodies. */
 int nbody_accel_variant_for_n(int64_t n);

@@ -329,3 +329,18 @@ def test_range_eighth_share_of_plummer1m():
     ref = ref_accel(pm, w.G, w.eps2, i0 + local)
     assert np.all(a[:, 3] == 0)
     assert_parity(a[local], ref, "1/8 share of plummer1m")
+
+
+@pytest.mark.parametrize("stream_v,lds_v", [(20, 1), (21, 2), (22, 1), (23, 2)])
+def test_lds_free_variants_bitwise_equal_lds(stream_v, lds_v):
+    """Same K, tile and j order, no LDS: identical sums, bit for bit."""
+    a = nb.nbody_accel_variant_info(stream_v)
+    b = nb.nbody_accel_variant_info(lds_v)
+    assert a["staging"] != 0 and b["staging"] == 0 and b["split"] == 1
+    assert (a["bodies_per_lane"], a["tile"]) == (b["bodies_per_lane"], b["tile"])
+    for n in (1, 300, 4097):
+        pm, _ = workloads.uniform_cube(n, seed=40 + n)
+        assert np.array_equal(gpu_accel(pm, variant=stream_v), gpu_accel(pm, variant=lds_v)), n
+    pm, _ = workloads.uniform_cube(5000, seed=41)
+    assert np.array_equal(range_accel(pm, 700, 3000, variant=stream_v),
+                          gpu_accel(pm, variant=lds_v)[700:3700])
