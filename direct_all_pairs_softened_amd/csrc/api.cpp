@@ -312,6 +312,7 @@ int nbody_energy(const float *posmass, const float *vel, int64_t n, float G, flo
   if (!n_ok(n)) return NBODY_ERR_INVALID_ARG;
   if (int s = check_consts(G, eps2)) return s;
   if (n == 0) return NBODY_OK;  // stats_out is left untouched
+  if (nbody::energy_pair_tasks(n) > INT32_MAX) return NBODY_ERR_INVALID_ARG;
   if (!posmass || !vel || !stats_out) return NBODY_ERR_INVALID_ARG;
   if (!aligned(stats_out, 8)) return NBODY_ERR_ALIGNMENT;
   if (!aligned(posmass, 16) || !aligned(vel, 16)) return NBODY_ERR_ALIGNMENT;

@@ -9,6 +9,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 namespace nbody {
@@ -71,6 +72,22 @@ __device__ __forceinline__ float pair_rsq(float xj, float yj, float zj, float xi
   d2 = __builtin_fmaf(dy, dy, d2);
   d2 = __builtin_fmaf(dz, dz, d2);
   return __builtin_amdgcn_rsqf(d2);
+}
+
+// Lane l receives lane l - 1's value (lane 0 receives lane 63's): one step of
+// the rotation that carries a j-body around the wavefront (DPP wave_ror:1).
+__device__ __forceinline__ float rotate_lanes(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x13C, 0xf, 0xf, false));
+}
+
+// Panel pair (I, J), I <= J, enumerated as t = J (J + 1) / 2 + I.
+__device__ __forceinline__ void decode_panel_pair(long long t, int &I, int &J) {
+  long long j = (long long)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
+  while (j * (j + 1) / 2 > t) --j;
+  while ((j + 1) * (j + 2) / 2 <= t) ++j;
+  J = (int)j;
+  I = (int)(t - j * (j + 1) / 2);
 }
 
 // ---------------------------------------------------------------------------

@@ -71,6 +71,7 @@ hipError_t launch_kick(float *vel, const float *accel, float h, int n, hipStream
 
 // Energy.
 size_t energy_workspace_bytes(int64_t n);
+int64_t energy_pair_tasks(int64_t n);  // blocks of the pair pass
 size_t energy_from_potential_workspace_bytes(int64_t n);
 hipError_t launch_energy_from_potential(const float *posmass, const float *vel,
                                         const float *accel, int n, void *workspace,

@@ -29,20 +29,12 @@
 // Per pair (two interactions) a lane issues 16 FP32 VALU ops and one
 // v_rsq_f32, plus 7 / K DPP moves; the one-sided kernel issues 12 ops and one
 // v_rsq_f32 per interaction.
-#include <math.h>
-
 #include "nbody_common.hpp"
 #include "nbody_internal.hpp"
 
 namespace nbody {
 
 namespace {
-
-// Lane l receives lane l - 1's value (lane 0 receives lane 63's).
-__device__ __forceinline__ float rotate_lanes(float v) {
-  return __int_as_float(
-      __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x13C, 0xf, 0xf, false));
-}
 
 template <int K, int KP, int W, bool DIAG>
 __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, int I, int J,
@@ -159,12 +151,8 @@ __global__ __launch_bounds__(W *kWave) __attribute__((amdgpu_waves_per_eu(OCC)))
 symmetric_task_kernel(const float4 *__restrict__ pm, int n, int P, float eps2,
                       float *__restrict__ part) {
   __shared__ float csum[W][KP][3][kWave];
-  const long long t = blockIdx.x;
-  long long J = (long long)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
-  while (J * (J + 1) / 2 > t) --J;
-  while ((J + 1) * (J + 2) / 2 <= t) ++J;
-  const int Jc = (int)J;
-  const int Ic = (int)(t - J * (J + 1) / 2);
+  int Ic, Jc;
+  decode_panel_pair(blockIdx.x, Ic, Jc);
   if (Ic == Jc)
     sym_task<K, KP, W, true>(pm, n, Ic, Jc, P, eps2, part, csum);
   else

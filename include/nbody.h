@@ -225,9 +225,11 @@ int nbody_kick(float *vel, const float *accel, float h, int64_t n,
  * with K = sum m |v|^2 / 2, P = sum m v, M = sum m and
  * W = -G sum_{i<j} m_i m_j / sqrt(|x_i - x_j|^2 + eps^2), the softened
  * potential whose negative gradient is the acceleration above (the pages
- * print no energy; this is the plain reading).  Pair terms are fp32 (the
- * j = i term is excluded by an index test); per-body sums go to fp64 per
- * tile and every cross-body sum is fp64 in a fixed tree order.
+ * print no energy; this is the plain reading).  W is summed over panel pairs
+ * with every unordered pair met once (as in nbody_accel_symmetric): pair
+ * terms in fp32 over 64-body sweeps, then fp64, and every cross-lane,
+ * cross-task and cross-body sum in a fixed fp64 tree order.  n above about
+ * 1.3e8 (more than 2^31 - 1 panel pairs) is NBODY_ERR_INVALID_ARG.
  *   workspace  >= nbody_energy_workspace_bytes(n) bytes, 16-byte aligned,
  *              disjoint from every other argument.
  *   stats_out  8 doubles, 8-byte aligned. */
