@@ -36,7 +36,55 @@ namespace nbody {
 
 namespace {
 
-template <int K, int KP, int W, bool DIAG>
+// One step of the off-diagonal sweep: the lane's K i-bodies against its
+// current j-body.  The pairs are processed IL at a time in phases (all
+// differences, then all d^2, all rsq, ...), which gives each wave IL
+// independent chains to issue from; IL = 1 is one pair after the other.  The
+// arithmetic of each pair, and its order of accumulation, do not depend on IL.
+template <int K, int IL>
+__device__ __forceinline__ void sym_step(const float (&xi)[K], const float (&yi)[K],
+                                         const float (&zi)[K], const float (&mi)[K], float xj,
+                                         float yj, float zj, float mj, float eps2, float (&ax)[K],
+                                         float (&ay)[K], float (&az)[K], float &cx, float &cy,
+                                         float &cz) {
+  static_assert(K % IL == 0, "interleave width must divide K");
+#pragma unroll
+  for (int h = 0; h < K; h += IL) {
+    float dx[IL], dy[IL], dz[IL], w[IL];
+#pragma unroll
+    for (int q = 0; q < IL; ++q) {
+      dx[q] = xj - xi[h + q];
+      dy[q] = yj - yi[h + q];
+      dz[q] = zj - zi[h + q];
+    }
+#pragma unroll
+    for (int q = 0; q < IL; ++q) w[q] = __builtin_fmaf(dx[q], dx[q], eps2);
+#pragma unroll
+    for (int q = 0; q < IL; ++q) w[q] = __builtin_fmaf(dy[q], dy[q], w[q]);
+#pragma unroll
+    for (int q = 0; q < IL; ++q) w[q] = __builtin_fmaf(dz[q], dz[q], w[q]);
+#pragma unroll
+    for (int q = 0; q < IL; ++q) w[q] = __builtin_amdgcn_rsqf(w[q]);
+#pragma unroll
+    for (int q = 0; q < IL; ++q) w[q] = (w[q] * w[q]) * w[q];
+#pragma unroll
+    for (int q = 0; q < IL; ++q) {
+      const float sj = mj * w[q];
+      ax[h + q] = __builtin_fmaf(sj, dx[q], ax[h + q]);
+      ay[h + q] = __builtin_fmaf(sj, dy[q], ay[h + q]);
+      az[h + q] = __builtin_fmaf(sj, dz[q], az[h + q]);
+    }
+#pragma unroll
+    for (int q = 0; q < IL; ++q) {
+      const float si = mi[h + q] * w[q];
+      cx = __builtin_fmaf(si, dx[q], cx);
+      cy = __builtin_fmaf(si, dy[q], cy);
+      cz = __builtin_fmaf(si, dz[q], cz);
+    }
+  }
+}
+
+template <int K, int KP, int W, int IL, bool DIAG>
 __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, int I, int J,
                                          int P, float eps2, float *__restrict__ part,
                                          float (*csum)[KP][3][kWave]) {
@@ -78,6 +126,10 @@ __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, i
     for (int s = 0; s < kWave; ++s) {
 #pragma unroll
       for (int p = 0; p < KP; ++p) {
+        if constexpr (!DIAG) {
+          sym_step<K, IL>(xi, yi, zi, mi, xj[p], yj[p], zj[p], mj[p], eps2, ax, ay, az, cx[p],
+                          cy[p], cz[p]);
+        } else {
 #pragma unroll
         for (int q = 0; q < K; ++q) {
           const float dx = xj[p] - xi[q];
@@ -87,22 +139,11 @@ __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, i
           d2 = __builtin_fmaf(dy, dy, d2);
           d2 = __builtin_fmaf(dz, dz, d2);
           const float inv = __builtin_amdgcn_rsqf(d2);
-          if constexpr (DIAG) {
-            const float sj = (mj[p] * inv) * (inv * inv);
-            ax[q] = __builtin_fmaf(sj, dx, ax[q]);
-            ay[q] = __builtin_fmaf(sj, dy, ay[q]);
-            az[q] = __builtin_fmaf(sj, dz, az[q]);
-          } else {
-            const float w = (inv * inv) * inv;
-            const float sj = mj[p] * w;
-            ax[q] = __builtin_fmaf(sj, dx, ax[q]);
-            ay[q] = __builtin_fmaf(sj, dy, ay[q]);
-            az[q] = __builtin_fmaf(sj, dz, az[q]);
-            const float si = mi[q] * w;
-            cx[p] = __builtin_fmaf(si, dx, cx[p]);
-            cy[p] = __builtin_fmaf(si, dy, cy[p]);
-            cz[p] = __builtin_fmaf(si, dz, cz[p]);
-          }
+          const float sj = (mj[p] * inv) * (inv * inv);
+          ax[q] = __builtin_fmaf(sj, dx, ax[q]);
+          ay[q] = __builtin_fmaf(sj, dy, ay[q]);
+          az[q] = __builtin_fmaf(sj, dz, az[q]);
+        }
         }
         xj[p] = rotate_lanes(xj[p]);
         yj[p] = rotate_lanes(yj[p]);
@@ -146,7 +187,7 @@ __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, i
 }
 
 // One block per task; blockIdx.x = J (J + 1) / 2 + I enumerates I <= J.
-template <int K, int KP, int W, int OCC>
+template <int K, int KP, int W, int OCC, int IL>
 __global__ __launch_bounds__(W *kWave) __attribute__((amdgpu_waves_per_eu(OCC))) void
 symmetric_task_kernel(const float4 *__restrict__ pm, int n, int P, float eps2,
                       float *__restrict__ part) {
@@ -154,9 +195,9 @@ symmetric_task_kernel(const float4 *__restrict__ pm, int n, int P, float eps2,
   int Ic, Jc;
   decode_panel_pair(blockIdx.x, Ic, Jc);
   if (Ic == Jc)
-    sym_task<K, KP, W, true>(pm, n, Ic, Jc, P, eps2, part, csum);
+    sym_task<K, KP, W, IL, true>(pm, n, Ic, Jc, P, eps2, part, csum);
   else
-    sym_task<K, KP, W, false>(pm, n, Ic, Jc, P, eps2, part, csum);
+    sym_task<K, KP, W, IL, false>(pm, n, Ic, Jc, P, eps2, part, csum);
 }
 
 __global__ __launch_bounds__(256) void symmetric_reduce_kernel(const float *__restrict__ part,
@@ -175,27 +216,32 @@ __global__ __launch_bounds__(256) void symmetric_reduce_kernel(const float *__re
   out[i] = make_float4(G * sx, G * sy, G * sz, 0.0f);
 }
 
-// (id, K, KP, waves, occupancy target); panel B = 64 * waves * K.
+// (id, K, KP, waves, occupancy target, interleave width); panel B =
+// 64 * waves * K.  Interleave widths 2 and 4 (variants 12, 13) measured the
+// same as 1 on MI355X: under the 6-waves-per-SIMD register budget the
+// compiler schedules the pairs one after the other either way.
 #define NBODY_SYM_VARIANTS(X) \
-  X(0, 8, 2, 4, 4)            \
-  X(1, 8, 1, 4, 4)            \
-  X(2, 4, 2, 4, 6)            \
-  X(3, 8, 2, 8, 4)            \
-  X(4, 4, 4, 4, 4)            \
-  X(5, 8, 1, 8, 4)            \
-  X(6, 16, 1, 4, 2)           \
-  X(7, 12, 1, 4, 3)           \
-  X(8, 8, 1, 2, 4)            \
-  X(9, 8, 1, 4, 6)            \
-  X(10, 6, 1, 4, 5)           \
-  X(11, 16, 1, 2, 2)
+  X(0, 8, 2, 4, 4, 1)         \
+  X(1, 8, 1, 4, 4, 1)         \
+  X(2, 4, 2, 4, 6, 1)         \
+  X(3, 8, 2, 8, 4, 1)         \
+  X(4, 4, 4, 4, 4, 1)         \
+  X(5, 8, 1, 8, 4, 1)         \
+  X(6, 16, 1, 4, 2, 1)        \
+  X(7, 12, 1, 4, 3, 1)        \
+  X(8, 8, 1, 2, 4, 1)         \
+  X(9, 8, 1, 4, 6, 1)         \
+  X(10, 6, 1, 4, 5, 1)        \
+  X(11, 16, 1, 2, 2, 1)       \
+  X(12, 8, 1, 4, 6, 4)        \
+  X(13, 8, 1, 4, 6, 2)
 
 struct SymVariant {
   int K, KP, W;
 };
 
 const SymVariant kSym[] = {
-#define X(id, K, KP, W, OCC) {K, KP, W},
+#define X(id, K, KP, W, OCC, IL) {K, KP, W},
     NBODY_SYM_VARIANTS(X)
 #undef X
 };
@@ -232,9 +278,9 @@ hipError_t launch_symmetric(const float *posmass, int n, float G, float eps2, fl
   float *part = reinterpret_cast<float *>(workspace);
   const float4 *pm = reinterpret_cast<const float4 *>(posmass);
   switch (v) {
-#define X(id, K, KP, W, OCC)                                                              \
+#define X(id, K, KP, W, OCC, IL)                                                          \
   case id:                                                                                \
-    hipLaunchKernelGGL((symmetric_task_kernel<K, KP, W, OCC>), dim3((unsigned)tasks),     \
+    hipLaunchKernelGGL((symmetric_task_kernel<K, KP, W, OCC, IL>), dim3((unsigned)tasks), \
                        dim3(W * kWave), 0, stream, pm, n, P, eps2, part);                 \
     break;
     NBODY_SYM_VARIANTS(X)

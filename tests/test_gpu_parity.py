@@ -344,3 +344,60 @@ def test_lds_free_variants_bitwise_equal_lds(stream_v, lds_v):
     pm, _ = workloads.uniform_cube(5000, seed=41)
     assert np.array_equal(range_accel(pm, 700, 3000, variant=stream_v),
                           gpu_accel(pm, variant=lds_v)[700:3700])
+
+
+def test_symmetric_interleave_variants_bitwise_equal():
+    """Variants that differ only in the issue order of independent pairs
+    (interleave width) compute the same sums."""
+    pm, _ = workloads.uniform_cube(6000, seed=55, masses="lognormal")
+    base = sym_accel(pm, eps2=1e-5, variant=9)
+    for v in (12, 13):
+        assert nb.nbody_accel_symmetric_panel(v) == nb.nbody_accel_symmetric_panel(9)
+        assert np.array_equal(sym_accel(pm, eps2=1e-5, variant=v), base), v
+
+
+# ---------------------------------------------------------------------------
+# Degenerate inputs
+# ---------------------------------------------------------------------------
+
+def test_empty_input_is_a_no_op():
+    empty = torch.empty((0, 4), device=DEV)
+    out = torch.empty((0, 4), device=DEV)
+    nb.nbody_accel(empty, 1.0, 1e-4, out)
+    ws = torch.empty(16, dtype=torch.uint8, device=DEV)
+    nb.nbody_accel_symmetric(empty, 1.0, 1e-4, out, ws)
+    nb.nbody_leapfrog_step(empty, torch.empty((0, 4), device=DEV), out, 1e-3)
+    stats = torch.full((8,), 7.0, dtype=torch.float64, device=DEV)
+    nb.nbody_energy(empty, torch.empty((0, 4), device=DEV), 1.0, 1e-4, ws, stats)
+    torch.cuda.synchronize()
+    assert stats.cpu().tolist() == [7.0] * 8     # n == 0 touches nothing
+
+
+@pytest.mark.parametrize("path", ["tile", "symmetric"])
+def test_all_bodies_coincident_and_massless(path):
+    n = 3000
+    acc = gpu_accel if path == "tile" else sym_accel
+    pm = np.zeros((n, 4), F32)
+    pm[:, :3] = (0.25, -0.5, 0.75)
+    pm[:, 3] = 1.0 / n
+    assert np.array_equal(acc(pm), np.zeros((n, 4), F32))       # r = 0 for every pair
+    pm, _ = workloads.uniform_cube(n, seed=60)
+    pm[:, 3] = 0.0
+    assert np.array_equal(acc(pm), np.zeros((n, 4), F32))       # no mass, no force
+
+
+@pytest.mark.parametrize("path", ["tile", "symmetric"])
+def test_one_massive_body_among_test_particles(path):
+    """Massless bodies feel only the massive one: a_i = G M r / (r^2+eps^2)^{3/2};
+    the massive body feels nothing (every other mass is zero)."""
+    n, M, G, eps2 = 5000, 3.0, 0.7, 1e-3
+    pm, _ = workloads.uniform_cube(n, seed=61)
+    pm[:, 3] = 0.0
+    pm[1234] = (0.1, 0.2, -0.3, M)
+    a = gpu_accel(pm, G, eps2) if path == "tile" else sym_accel(pm, G, eps2)
+    assert np.array_equal(a[1234], np.zeros(4, F32))
+    d = pm[1234, :3].astype(np.float64) - pm[:, :3].astype(np.float64)
+    e = float(F32(eps2))
+    expect = float(F32(G)) * M * d / ((d * d).sum(axis=1) + e)[:, None] ** 1.5
+    expect[1234] = 0.0
+    assert_parity(a, expect, f"test particles {path}")
