@@ -43,7 +43,7 @@ __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1))) void force_tile_kernel(
   constexpr int LOADS = (S * T) / NTHREADS;
   static_assert(WAVES % S == 0, "waves must be a multiple of the split");
   static_assert((S * T) % NTHREADS == 0, "staged bodies must divide evenly over threads");
-  static_assert(S == 1 || GW * K * 3 * kWave <= 2 * S * T * 4,
+  static_assert(S == 1 || GW * K * (POT ? 4 : 3) * kWave <= 2 * S * T * 4,
                 "one part's sums must fit in the tile buffers");
   __shared__ float4 tile[2][S * T];
 
@@ -135,40 +135,60 @@ __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1))) void force_tile_kernel(
   }
 
   if constexpr (S > 1) {
-    // Part p's sums go through the (now idle) tile buffer one part at a time
-    // and part 0 adds them in ascending p.
     float *red = reinterpret_cast<float *>(&tile[0][0]);
-    for (int p = 1; p < S; ++p) {
+    constexpr int NC = POT ? 4 : 3;  // sums per body
+    if constexpr ((S - 1) * GW * K * NC * kWave <= 2 * S * T * 4) {
+      // All parts p >= 1 write their sums into the (now idle) tile buffers at
+      // once; after one barrier part 0 adds them in ascending p.
       __syncthreads();
-      if (part == p) {
+      if (part > 0) {
 #pragma unroll
         for (int q = 0; q < K; ++q) {
-          const int o = ((grp * K + q) * 3) * kWave + lane;
+          const int o = (((part - 1) * GW + grp) * K + q) * NC * kWave + lane;
           red[o] = ax[q];
           red[o + kWave] = ay[q];
           red[o + 2 * kWave] = az[q];
+          if constexpr (POT) red[o + 3 * kWave] = ap[q];
         }
       }
       __syncthreads();
       if (part == 0) {
+        for (int p = 1; p < S; ++p) {
 #pragma unroll
-        for (int q = 0; q < K; ++q) {
-          const int o = ((grp * K + q) * 3) * kWave + lane;
-          ax[q] += red[o];
-          ay[q] += red[o + kWave];
-          az[q] += red[o + 2 * kWave];
+          for (int q = 0; q < K; ++q) {
+            const int o = (((p - 1) * GW + grp) * K + q) * NC * kWave + lane;
+            ax[q] += red[o];
+            ay[q] += red[o + kWave];
+            az[q] += red[o + 2 * kWave];
+            if constexpr (POT) ap[q] += red[o + 3 * kWave];
+          }
         }
       }
-      if constexpr (POT) {
+    } else {
+      // Part p's sums go through the tile buffers one part at a time and
+      // part 0 adds them in ascending p.
+      for (int p = 1; p < S; ++p) {
         __syncthreads();
         if (part == p) {
 #pragma unroll
-          for (int q = 0; q < K; ++q) red[(grp * K + q) * kWave + lane] = ap[q];
+          for (int q = 0; q < K; ++q) {
+            const int o = ((grp * K + q) * NC) * kWave + lane;
+            red[o] = ax[q];
+            red[o + kWave] = ay[q];
+            red[o + 2 * kWave] = az[q];
+            if constexpr (POT) red[o + 3 * kWave] = ap[q];
+          }
         }
         __syncthreads();
         if (part == 0) {
 #pragma unroll
-          for (int q = 0; q < K; ++q) ap[q] += red[(grp * K + q) * kWave + lane];
+          for (int q = 0; q < K; ++q) {
+            const int o = ((grp * K + q) * NC) * kWave + lane;
+            ax[q] += red[o];
+            ay[q] += red[o + kWave];
+            az[q] += red[o + 2 * kWave];
+            if constexpr (POT) ap[q] += red[o + 3 * kWave];
+          }
         }
       }
     }
