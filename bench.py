@@ -86,6 +86,9 @@ def cpu_baseline(pm_np, acc0_np, w, seconds):
 
 
 SPLITJ_CHUNKS = (32, 256, 1024, 4096, 16384)
+# (j_chunk, terms) of the tree first pass: the README's 32-wide block as a
+# plain tree, FADL and fadl4, then wider trees
+SPLITJ_TREES = ((32, 1), (32, 2), (32, 4), (64, 1), (64, 2), (128, 2), (256, 4))
 SPLITJ_MAX_WORKSPACE = 16 << 30
 
 
@@ -148,6 +151,15 @@ def sweep(nb, torch, w, pm, acc, reps, paths):
         ws = torch.empty(need, dtype=torch.uint8, device=pm.device)
         ms = _time(torch, lambda: nb.nbody_accel_splitj(pm, w.G, w.eps2, acc, j_chunk, ws), reps)
         _sweep_line(w, ms, splitj_chunk=j_chunk, workspace_bytes=need)
+        del ws
+    for j_chunk, terms in SPLITJ_TREES if "splitj" in paths else ():
+        need = nb.nbody_accel_splitj_tree_workspace_bytes(w.n, j_chunk, terms)
+        if need > SPLITJ_MAX_WORKSPACE or -(-w.n // j_chunk) > 65535:
+            continue
+        ws = torch.empty(need, dtype=torch.uint8, device=pm.device)
+        ms = _time(torch, lambda: nb.nbody_accel_splitj_tree(pm, w.G, w.eps2, acc, j_chunk, terms,
+                                                             ws), reps)
+        _sweep_line(w, ms, splitj_tree_chunk=j_chunk, terms=terms, workspace_bytes=need)
         del ws
 
 

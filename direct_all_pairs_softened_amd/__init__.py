@@ -36,6 +36,7 @@ EXPORTS = (
     "nbody_accel_range", "nbody_accel_potential",
     "nbody_energy_from_potential", "nbody_energy_from_potential_workspace_bytes",
     "nbody_accel_splitj", "nbody_accel_splitj_workspace_bytes",
+    "nbody_accel_splitj_tree", "nbody_accel_splitj_tree_workspace_bytes",
     "nbody_accel_symmetric", "nbody_accel_symmetric_workspace_bytes",
     "nbody_accel_symmetric_variant_count", "nbody_accel_symmetric_panel",
     "nbody_accel_symmetric_variant_for_n",
@@ -84,6 +85,9 @@ def load_library(path: str | None = None):
         "nbody_accel_range": (c_int, [vp, c_i64, c_i64, c_i64, c_f, c_f, vp, c_int, vp]),
         "nbody_accel_splitj": (c_int, [vp, c_i64, c_f, c_f, vp, c_i64, vp, c_sz, vp]),
         "nbody_accel_splitj_workspace_bytes": (c_sz, [c_i64, c_i64]),
+        "nbody_accel_splitj_tree": (c_int, [vp, c_i64, c_f, c_f, vp, c_i64, c_int, vp, c_sz,
+                                            vp]),
+        "nbody_accel_splitj_tree_workspace_bytes": (c_sz, [c_i64, c_i64, c_int]),
         "nbody_accel_symmetric": (c_int, [vp, c_i64, c_f, c_f, vp, c_int, vp, c_sz, vp]),
         "nbody_accel_symmetric_workspace_bytes": (c_sz, [c_i64, c_int]),
         "nbody_accel_symmetric_variant_count": (c_int, []),
@@ -252,6 +256,25 @@ def nbody_accel_splitj(posmass, G: float, eps2: float, accel_out, j_chunk: int, 
                                              _f32(accel_out, "accel_out", (4,)), int(j_chunk),
                                              ws, nbytes, _stream(stream)),
            "nbody_accel_splitj")
+
+
+def nbody_accel_splitj_tree_workspace_bytes(n: int, j_chunk: int, terms: int) -> int:
+    return int(load_library().nbody_accel_splitj_tree_workspace_bytes(int(n), int(j_chunk),
+                                                                      int(terms)))
+
+
+def nbody_accel_splitj_tree(posmass, G: float, eps2: float, accel_out, j_chunk: int, terms: int,
+                            workspace, stream=None):
+    n = _n_of(posmass)
+    if _n_of(accel_out) != n:
+        raise ValueError("accel_out must have N rows")
+    ws = _dev(workspace, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load_library().nbody_accel_splitj_tree(_f32(posmass, "posmass", (4,)), n, G, eps2,
+                                                  _f32(accel_out, "accel_out", (4,)),
+                                                  int(j_chunk), int(terms), ws, nbytes,
+                                                  _stream(stream)),
+           "nbody_accel_splitj_tree")
 
 
 def nbody_accel_symmetric_workspace_bytes(n: int, variant: int = -1) -> int:

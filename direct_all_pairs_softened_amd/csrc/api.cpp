@@ -209,6 +209,33 @@ int nbody_accel_splitj(const float *posmass, int64_t n, float G, float eps2, flo
                                          workspace, as_stream(stream)));
 }
 
+size_t nbody_accel_splitj_tree_workspace_bytes(int64_t n, int64_t j_chunk, int terms) {
+  if (!n_ok(n)) return 0;
+  return nbody::splitj_tree_workspace_bytes(n, j_chunk, terms);
+}
+
+int nbody_accel_splitj_tree(const float *posmass, int64_t n, float G, float eps2,
+                            float *accel_out, int64_t j_chunk, int terms, void *workspace,
+                            size_t workspace_bytes, void *stream) {
+  if (!n_ok(n)) return NBODY_ERR_INVALID_ARG;
+  if (int s = check_consts(G, eps2)) return s;
+  if (!nbody::splitj_tree_shape_ok(j_chunk, terms)) return NBODY_ERR_INVALID_ARG;
+  if (n == 0) return NBODY_OK;
+  // the chunk index is the grid's y dimension
+  if ((n + j_chunk - 1) / j_chunk > 65535) return NBODY_ERR_INVALID_ARG;
+  if (!posmass || !accel_out) return NBODY_ERR_INVALID_ARG;
+  if (!aligned(posmass, 16) || !aligned(accel_out, 16)) return NBODY_ERR_ALIGNMENT;
+  const size_t need = nbody::splitj_tree_workspace_bytes(n, j_chunk, terms);
+  if (!workspace || workspace_bytes < need) return NBODY_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return NBODY_ERR_ALIGNMENT;
+  const size_t bytes = (size_t)n * 16;
+  if (overlap(posmass, bytes, accel_out, bytes) || overlap(workspace, need, posmass, bytes) ||
+      overlap(workspace, need, accel_out, bytes))
+    return NBODY_ERR_ALIAS;
+  return hip_status(nbody::launch_splitj_tree(posmass, (int)n, G, eps2, accel_out, (int)j_chunk,
+                                              terms, workspace, as_stream(stream)));
+}
+
 static int sym_variant(int v, int64_t n) { return v < 0 ? nbody::symmetric_variant_for_n(n) : v; }
 
 int nbody_accel_symmetric_variant_count(void) { return nbody::symmetric_variant_count(); }

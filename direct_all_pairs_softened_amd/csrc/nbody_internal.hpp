@@ -54,6 +54,10 @@ hipError_t launch_force_potential(const float *posmass, int n, float G, float ep
 size_t splitj_workspace_bytes(int64_t n, int64_t j_chunk);
 hipError_t launch_splitj(const float *posmass, int n, float G, float eps2, float *accel,
                          int j_chunk, void *workspace, hipStream_t stream);
+bool splitj_tree_shape_ok(int64_t j_chunk, int terms);
+size_t splitj_tree_workspace_bytes(int64_t n, int64_t j_chunk, int terms);
+hipError_t launch_splitj_tree(const float *posmass, int n, float G, float eps2, float *accel,
+                              int j_chunk, int terms, void *workspace, hipStream_t stream);
 
 // Pair-symmetric force pass (each pair once, applied to both bodies).
 int symmetric_variant_count();

@@ -158,6 +158,33 @@ int nbody_accel_splitj(const float *posmass, int64_t n, float G, float eps2,
  * j_chunk). */
 size_t nbody_accel_splitj_workspace_bytes(int64_t n, int64_t j_chunk);
 
+/* Two-pass decomposition with a tree in the first pass (the README's
+ * section 3.2 block, and the "first add during load" change of its section
+ * 3.4).  A group of X = j_chunk / terms lanes owns one body i and one chunk
+ * of j_chunk j-bodies: each lane adds `terms` pair terms in registers (j =
+ * c j_chunk + f X + lane, f ascending), then the group halves its width
+ * (lane x adds lane x + stride, stride = X/2, ..., 1) and lane 0 writes the
+ * chunk's float4 partial; the second pass is nbody_accel_splitj's (chunks in
+ * ascending order, times G).  Results are bitwise reproducible for a given
+ * (j_chunk, terms) and agree with the other passes to rounding.
+ *   terms      1 (plain tree), 2 (FADL) or 4 (fadl4).
+ *   j_chunk    terms * X with X one of 8, 16, 32, 64; the README's 32-wide
+ *              block is j_chunk = 32 with X = 32, 16, 8 for terms 1, 2, 4.
+ *              The chunk count ceil(n / j_chunk) must be <= 65535.
+ *   workspace  >= nbody_accel_splitj_tree_workspace_bytes(n, j_chunk, terms)
+ *              bytes (ceil(n / j_chunk) * n float4), 16-byte aligned,
+ *              disjoint from posmass and accel_out; contents on return are
+ *              unspecified.
+ * Other arguments as nbody_accel; NBODY_ERR_INVALID_ARG for any other
+ * (j_chunk, terms). */
+int nbody_accel_splitj_tree(const float *posmass, int64_t n, float G, float eps2,
+                            float *accel_out, int64_t j_chunk, int terms, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/* Workspace bytes nbody_accel_splitj_tree needs (0 for n == 0 or an invalid
+ * (j_chunk, terms)). */
+size_t nbody_accel_splitj_tree_workspace_bytes(int64_t n, int64_t j_chunk, int terms);
+
 /* Pair-symmetric force pass: each unordered pair is evaluated once and its
  * term is applied to both bodies (Newton's third law).  The atomics tutorial
  * ("CUDA programming (9)", neighbour-list example) runs this symmetric half

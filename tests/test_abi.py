@@ -137,6 +137,44 @@ def test_splitj_validation(lib):
     assert f(vp(A), 0, 1.0, 1e-4, vp(B), 32, None, 0, None) == nb.NBODY_OK
 
 
+def test_splitj_tree_shapes_and_validation(lib):
+    ws = nb.nbody_accel_splitj_tree_workspace_bytes
+    # the README's 32-wide block: plain tree, FADL and fadl4
+    for terms in (1, 2, 4):
+        assert ws(131072, 32, terms) == 4096 * 131072 * 16
+    assert ws(1000, 256, 4) == 4 * 1000 * 16          # X = 64
+    assert ws(1000, 8, 1) == 125 * 1000 * 16          # X = 8
+    assert ws(1000, 4, 1) == 0                        # X = 4 below the smallest tree
+    assert ws(1000, 128, 1) == 0                      # X = 128 wider than a wavefront
+    assert ws(1000, 48, 2) == 0                       # X = 24 not a power of two
+    assert ws(1000, 32, 3) == 0                       # terms not 1, 2 or 4
+    assert ws(0, 32, 1) == 0
+    f = lib.nbody_accel_splitj_tree
+    need = ws(1000, 32, 2)
+    ok = (vp(A), 1000, 1.0, 1e-4, vp(B), 32, 2, vp(C), need, None)
+
+    def call(**kw):
+        names = ("pm", "n", "G", "eps2", "out", "chunk", "terms", "ws", "bytes", "stream")
+        args = dict(zip(names, ok))
+        args.update(kw)
+        return f(*[args[k] for k in names])
+
+    assert call(terms=3) == nb.NBODY_ERR_INVALID_ARG
+    assert call(chunk=48) == nb.NBODY_ERR_INVALID_ARG
+    assert call(chunk=256, terms=1) == nb.NBODY_ERR_INVALID_ARG
+    assert call(eps2=0.0) == nb.NBODY_ERR_INVALID_ARG
+    assert call(pm=None) == nb.NBODY_ERR_INVALID_ARG
+    assert call(ws=None) == nb.NBODY_ERR_WORKSPACE
+    assert call(bytes=need - 1) == nb.NBODY_ERR_WORKSPACE
+    assert call(ws=vp(C + 8)) == nb.NBODY_ERR_ALIGNMENT
+    assert call(out=vp(B + 4)) == nb.NBODY_ERR_ALIGNMENT
+    assert call(ws=vp(A)) == nb.NBODY_ERR_ALIAS
+    assert call(out=vp(A + 16)) == nb.NBODY_ERR_ALIAS
+    # more than 65535 chunks
+    assert call(n=32 * 70000, bytes=1 << 62) == nb.NBODY_ERR_INVALID_ARG
+    assert call(n=0, pm=None, out=None, ws=None, bytes=0) == nb.NBODY_OK
+
+
 def test_integrator_validation(lib):
     lf = lib.nbody_leapfrog_step
     assert lf(vp(A), vp(B), vp(C), 1e-3, 0, None) == nb.NBODY_OK

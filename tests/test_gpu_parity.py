@@ -191,6 +191,56 @@ def test_splitj_lognormal128k_sampled_and_deterministic():
         assert_parity(outs[0][rows], ref, f"splitj lognormal128k J={j_chunk}")
 
 
+TREE_SHAPES = [(x * f, f) for f in (1, 2, 4) for x in (8, 16, 32, 64)]
+
+
+def tree_accel(pm_np, G=1.0, eps2=1e-4, j_chunk=32, terms=2):
+    t = torch.from_numpy(pm_np).to(DEV)
+    out = torch.full_like(t, float("nan"))
+    n = pm_np.shape[0]
+    ws = torch.empty(max(nb.nbody_accel_splitj_tree_workspace_bytes(n, j_chunk, terms), 16),
+                     dtype=torch.uint8, device=DEV)
+    nb.nbody_accel_splitj_tree(t, G, eps2, out, j_chunk, terms, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("j_chunk,terms", TREE_SHAPES)
+def test_splitj_tree_parity(j_chunk, terms):
+    """Tree first pass (plain, FADL, fadl4) at every tree width, on sizes that
+    leave a ragged last chunk and a ragged last block of i-bodies."""
+    for n in (1, 2, 65, 1000, 4097):
+        pm, _ = workloads.uniform_cube(n, seed=5)
+        log(f"splitj_tree n={n} J={j_chunk} F={terms}")
+        a = tree_accel(pm, j_chunk=j_chunk, terms=terms)
+        assert np.all(a[:, 3] == 0)
+        if n == 1:
+            assert np.array_equal(a, np.zeros((1, 4), F32))
+        else:
+            assert_parity(a, ref_accel(pm), f"splitj_tree n={n} J={j_chunk} F={terms}")
+
+
+def test_splitj_tree_lognormal128k_sampled_and_deterministic():
+    """The README's 32-wide block at the 131072-body workload: plain tree,
+    FADL and fadl4, each run twice."""
+    w = workloads.WORKLOADS["lognormal128k"]
+    pm, _ = workloads.make("lognormal128k")
+    rows = sample_rows(w.n, 512, seed=4)
+    ref = ref_accel(pm, w.G, w.eps2, rows)
+    t = torch.from_numpy(pm).to(DEV)
+    ws = torch.empty(nb.nbody_accel_splitj_tree_workspace_bytes(w.n, 32, 1),
+                     dtype=torch.uint8, device=DEV)
+    for terms in (1, 2, 4):
+        outs = []
+        for _ in range(2):
+            out = torch.empty_like(t)
+            nb.nbody_accel_splitj_tree(t, w.G, w.eps2, out, 32, terms, ws)
+            torch.cuda.synchronize()
+            outs.append(out.cpu().numpy())
+        assert np.array_equal(outs[0], outs[1])
+        assert_parity(outs[0][rows], ref, f"splitj_tree lognormal128k F={terms}")
+
+
 def test_plummer1m_sampled_all_layouts():
     w = workloads.WORKLOADS["plummer1m"]
     pm, _ = workloads.make("plummer1m")
@@ -366,6 +416,7 @@ def test_empty_input_is_a_no_op():
     nb.nbody_accel(empty, 1.0, 1e-4, out)
     ws = torch.empty(16, dtype=torch.uint8, device=DEV)
     nb.nbody_accel_symmetric(empty, 1.0, 1e-4, out, ws)
+    nb.nbody_accel_splitj_tree(empty, 1.0, 1e-4, out, 32, 2, ws)
     nb.nbody_leapfrog_step(empty, torch.empty((0, 4), device=DEV), out, 1e-3)
     stats = torch.full((8,), 7.0, dtype=torch.float64, device=DEV)
     nb.nbody_energy(empty, torch.empty((0, 4), device=DEV), 1.0, 1e-4, ws, stats)
@@ -373,10 +424,14 @@ def test_empty_input_is_a_no_op():
     assert stats.cpu().tolist() == [7.0] * 8     # n == 0 touches nothing
 
 
-@pytest.mark.parametrize("path", ["tile", "symmetric"])
+PATHS = {"tile": lambda pm, *a: gpu_accel(pm, *a), "symmetric": lambda pm, *a: sym_accel(pm, *a),
+         "splitj_tree": lambda pm, *a: tree_accel(pm, *a)}
+
+
+@pytest.mark.parametrize("path", sorted(PATHS))
 def test_all_bodies_coincident_and_massless(path):
     n = 3000
-    acc = gpu_accel if path == "tile" else sym_accel
+    acc = PATHS[path]
     pm = np.zeros((n, 4), F32)
     pm[:, :3] = (0.25, -0.5, 0.75)
     pm[:, 3] = 1.0 / n
@@ -386,7 +441,7 @@ def test_all_bodies_coincident_and_massless(path):
     assert np.array_equal(acc(pm), np.zeros((n, 4), F32))       # no mass, no force
 
 
-@pytest.mark.parametrize("path", ["tile", "symmetric"])
+@pytest.mark.parametrize("path", sorted(PATHS))
 def test_one_massive_body_among_test_particles(path):
     """Massless bodies feel only the massive one: a_i = G M r / (r^2+eps^2)^{3/2};
     the massive body feels nothing (every other mass is zero)."""
@@ -394,7 +449,7 @@ def test_one_massive_body_among_test_particles(path):
     pm, _ = workloads.uniform_cube(n, seed=61)
     pm[:, 3] = 0.0
     pm[1234] = (0.1, 0.2, -0.3, M)
-    a = gpu_accel(pm, G, eps2) if path == "tile" else sym_accel(pm, G, eps2)
+    a = PATHS[path](pm, G, eps2)
     assert np.array_equal(a[1234], np.zeros(4, F32))
     d = pm[1234, :3].astype(np.float64) - pm[:, :3].astype(np.float64)
     e = float(F32(eps2))
