@@ -163,6 +163,127 @@ def sweep(nb, torch, w, pm, acc, reps, paths):
         del ws
 
 
+# timed force passes per workload in --suite (the benchmark spec's per-config reps)
+SUITE_REPS = {"uniform1k": 100, "plummer16k": 100, "lognormal128k": 50, "plummer1m": 10,
+              "collision1m": 5}
+
+
+def _stats(w, ms, interactions=None):
+    ms = sorted(ms)
+    med = ms[len(ms) // 2] if len(ms) % 2 else 0.5 * (ms[len(ms) // 2 - 1] + ms[len(ms) // 2])
+    inter = float(w.n) * float(w.n) if interactions is None else interactions
+    return {"reps": len(ms), "ms_median": med, "ms_min": ms[0],
+            "interactions_per_s_billions": inter / (med * 1e-3) / 1e9,
+            "pct_fp32_peak": 100 * FLOPS_PER_INTERACTION * inter / (med * 1e-3) / 1e12
+            / PEAK_FP32_TFLOPS}
+
+
+def suite(nb, torch, names):
+    """One JSON line per workload: force-pass times of the passes that apply
+    to it (median and min over the workload's reps), and for workloads with
+    dynamics the whole KDK run, timed once, with its energy drift and
+    momentum change measured by nbody_energy."""
+    import workloads
+    dev = torch.device("cuda:0")
+    for name in names:
+        w = workloads.WORKLOADS[name]
+        reps = SUITE_REPS[name]
+        log(f"suite {name}: {w.description}")
+        pm_np, vel_np = workloads.make(name)
+        pm = torch.from_numpy(pm_np).to(dev)
+        acc = torch.empty_like(pm)
+        out = {"workload": name, "n": w.n, "eps2": w.eps2}
+        force = {}
+        tv = nb.nbody_accel_variant_for_n(w.n)
+        force[f"one_sided_v{tv}"] = _stats(
+            w, _time(torch, lambda: nb.nbody_accel_variant(pm, w.G, w.eps2, acc, tv), reps))
+        sv = nb.nbody_accel_symmetric_variant_for_n(w.n)
+        sym_ws = torch.empty(max(nb.nbody_accel_symmetric_workspace_bytes(w.n, sv), 16),
+                             dtype=torch.uint8, device=dev)
+        force[f"symmetric_v{sv}"] = _stats(
+            w, _time(torch, lambda: nb.nbody_accel_symmetric(pm, w.G, w.eps2, acc, sym_ws, sv),
+                     reps))
+        if name == "plummer1m":
+            # the same one-sided arithmetic over 96-bit float3 records and SoA
+            pos3 = pm[:, :3].contiguous()
+            mass = pm[:, 3].contiguous()
+            acc3 = torch.empty_like(pos3)
+            force[f"one_sided_v{tv}_float3_aos"] = _stats(
+                w, _time(torch, lambda: nb.nbody_accel_f3aos(pos3, mass, w.G, w.eps2, acc3),
+                         reps))
+            xyz = [pm[:, k].contiguous() for k in range(4)]
+            axyz = [torch.empty_like(xyz[0]) for _ in range(3)]
+            force[f"one_sided_v{tv}_soa"] = _stats(
+                w, _time(torch, lambda: nb.nbody_accel_soa(*xyz, w.G, w.eps2, *axyz), reps))
+            del pos3, mass, acc3, xyz, axyz
+        if name == "lognormal128k":
+            for j_chunk in SPLITJ_CHUNKS:
+                ws = torch.empty(nb.nbody_accel_splitj_workspace_bytes(w.n, j_chunk),
+                                 dtype=torch.uint8, device=dev)
+                force[f"splitj_J{j_chunk}"] = _stats(
+                    w, _time(torch, lambda: nb.nbody_accel_splitj(pm, w.G, w.eps2, acc, j_chunk,
+                                                                  ws), reps))
+                del ws
+            for j_chunk, terms in SPLITJ_TREES:
+                ws = torch.empty(nb.nbody_accel_splitj_tree_workspace_bytes(w.n, j_chunk, terms),
+                                 dtype=torch.uint8, device=dev)
+                force[f"splitj_tree_J{j_chunk}_F{terms}"] = _stats(
+                    w, _time(torch, lambda: nb.nbody_accel_splitj_tree(pm, w.G, w.eps2, acc,
+                                                                       j_chunk, terms, ws), reps))
+                del ws
+        out["force"] = force
+        if w.steps > 0:
+            # the run uses whichever of the two passes was faster here
+            best = min(("one_sided", "symmetric"),
+                       key=lambda k: next(v["ms_median"] for f, v in force.items()
+                                          if f.startswith(k) and "_float3" not in f
+                                          and "_soa" not in f))
+            if best == "symmetric":
+                def fpass():
+                    nb.nbody_accel_symmetric(pm, w.G, w.eps2, acc, sym_ws, sv)
+            else:
+                def fpass():
+                    nb.nbody_accel_variant(pm, w.G, w.eps2, acc, tv)
+            vel = torch.from_numpy(vel_np).to(dev)
+            e0 = nb.energy(pm, vel, w.G, w.eps2)
+            fpass()
+            stream = torch.cuda.current_stream()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(w.steps + 1)]
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            ev[0].record(stream)
+            for k in range(w.steps):
+                nb.nbody_leapfrog_step(pm, vel, acc, w.dt)
+                fpass()
+                nb.nbody_kick(vel, acc, 0.5 * w.dt)
+                ev[k + 1].record(stream)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+            step_ms = [ev[k].elapsed_time(ev[k + 1]) for k in range(w.steps)]
+            e1 = nb.energy(pm, vel, w.G, w.eps2)
+            dp = sum((e1[c] - e0[c]) ** 2 for c in ("Px", "Py", "Pz")) ** 0.5
+            out["run"] = {"steps": w.steps, "dt": w.dt, "force_pass": best,
+                          "wall_s": wall, "step_ms_median": sorted(step_ms)[len(step_ms) // 2],
+                          "E0": e0["E"], "E1": e1["E"],
+                          "energy_drift": abs(e1["E"] - e0["E"]) / abs(e0["E"]),
+                          "momentum_change": dp}
+            del vel
+        if name == "plummer1m":
+            vel = torch.from_numpy(vel_np).to(dev)
+            sv_ws = sym_ws
+
+            def kdk():
+                nb.nbody_leapfrog_step(pm, vel, acc, w.dt)
+                nb.nbody_accel_symmetric(pm, w.G, w.eps2, acc, sv_ws, sv)
+                nb.nbody_kick(vel, acc, 0.5 * w.dt)
+            nb.nbody_accel_symmetric(pm, w.G, w.eps2, acc, sym_ws, sv)
+            out["kdk_step"] = _stats(w, _time(torch, kdk, 3))
+            del vel
+        print(json.dumps(out), flush=True)
+        del pm, acc, sym_ws
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,6 +301,9 @@ def main():
                     help="time the force pass of every compiled variant (one JSON line each) "
                          "instead of the step benchmark")
     ap.add_argument("--reps", type=int, default=3, help="timed force passes per variant (--sweep)")
+    ap.add_argument("--suite", default=None, metavar="NAMES",
+                    help="comma-separated workloads (or 'all'): per-workload force-pass times "
+                         "and whole KDK runs, one JSON line each, instead of the step benchmark")
     ap.add_argument("--sweep-paths", default="tile,symmetric,splitj",
                     help="comma-separated subset of tile, symmetric, splitj, range (--sweep)")
     args = ap.parse_args()
@@ -200,6 +324,11 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.suite:
+        names = (list(workloads.WORKLOADS) if args.suite == "all"
+                 else args.suite.split(","))
+        suite(nb, torch, names)
+        return
     w = workloads.WORKLOADS[args.workload]
     dt = w.dt if w.dt > 0 else 1e-4
     log(f"workload {w.name}: {w.description}")
