@@ -32,23 +32,25 @@ sys.path.insert(0, ROOT)
 FLOPS_PER_INTERACTION = 20          # "Cuda Nbody Notes", pair-step comments
 PEAK_FP32_TFLOPS = 157.3            # MI355X FP32 vector, 256 CU x 64 lanes x 2 x 2 x 2.4 GHz
 METRIC = "body-body interactions/s (billions), N=1M fp32; % of MI355X FP32 VALU peak"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "force_plummer1m_traffic.json")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def traffic_per_launch():
-    """HBM bytes per force launch from the committed counter summary, or None
-    when it is missing or was taken on a different kernel source."""
+def traffic_per_launch(path, variant, workload):
+    """HBM bytes per force launch from the committed counter record of this
+    force path, variant and workload, or None when there is none or it was
+    taken on a different kernel source."""
+    from direct_all_pairs_softened_amd.counters import kernel_source_hash, traffic_file
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(path, workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    from direct_all_pairs_softened_amd.counters import kernel_source_hash
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    if (t.get("path"), t.get("variant"), t.get("workload")) != (path, variant, workload):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash(path):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -402,7 +404,7 @@ def main():
     torch.cuda.synchronize()
     energy_ms = e0.elapsed_time(e1)
 
-    traffic = traffic_per_launch()
+    traffic = traffic_per_launch(args.path, variant, w.name)
     out = {
         "metric": METRIC,
         "value": value,

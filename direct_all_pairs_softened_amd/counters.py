@@ -28,16 +28,20 @@ from collections import defaultdict
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 COPY_BYTES = 1 << 30
-FORCE_KERNELS = ("symmetric_task_kernel", "force_tile_kernel")
+# the force kernel whose counters a record holds, per force path
+FORCE_KERNELS = {"symmetric": ("symmetric_task_kernel",), "tile": ("force_tile_kernel",)}
+# the sources that kernel is built from: a record is valid for a build only
+# while their hash matches
+KERNEL_SOURCES = {
+    "symmetric": ("direct_all_pairs_softened_amd/csrc/symmetric.hip",
+                  "direct_all_pairs_softened_amd/csrc/nbody_common.hpp"),
+    "tile": ("direct_all_pairs_softened_amd/csrc/force.hip",
+             "direct_all_pairs_softened_amd/csrc/nbody_common.hpp"),
+}
 COPY_KERNEL_HINTS = ("copyBuffer", "copy", "Copy")
-KERNEL_SOURCES = ("direct_all_pairs_softened_amd/csrc/force.hip",
-                  "direct_all_pairs_softened_amd/csrc/symmetric.hip",
-                  "direct_all_pairs_softened_amd/csrc/nbody_common.hpp")
-
-
-def kernel_source_hash() -> str:
+def kernel_source_hash(path: str) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[path]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -104,13 +108,20 @@ def algorithmic_bytes(kernel_name: str, n: int, panel: int) -> int:
     return 32 * n
 
 
+def traffic_file(path: str, workload: str) -> str:
+    """Where the counter record of a force path on a workload is kept."""
+    prefix = "force" if path == "symmetric" else "force_tile"
+    return os.path.join(ROOT, "profiles", f"{prefix}_{workload}_traffic.json")
+
+
 def cmd_summarize(args):
+    kernels = FORCE_KERNELS[args.path]
     fetch = read_counters(os.path.join(args.fetch_dir, "**", "*counter_collection.csv"))
     write = read_counters(os.path.join(args.write_dir, "**", "*counter_collection.csv"))
     copy_name, cf = pick(fetch, COPY_KERNEL_HINTS)
-    kname, ff = pick(fetch, FORCE_KERNELS)
+    kname, ff = pick(fetch, kernels)
     _, cw = pick(write, COPY_KERNEL_HINTS)
-    _, fw = pick(write, FORCE_KERNELS)
+    _, fw = pick(write, kernels)
     fetch_scale = COPY_BYTES / (cf["FETCH_SIZE"] * 1024.0)
     write_scale = COPY_BYTES / (cw["WRITE_SIZE"] * 1024.0)
     force_fetch = ff["FETCH_SIZE"] * 1024.0 * fetch_scale
@@ -118,8 +129,10 @@ def cmd_summarize(args):
     rec = {
         "workload": args.workload,
         "n": args.n,
+        "path": args.path,
+        "variant": args.variant,
         "kernel": kname,
-        "kernel_source_hash": kernel_source_hash(),
+        "kernel_source_hash": kernel_source_hash(args.path),
         "copy_kernel": copy_name,
         "copy_bytes": COPY_BYTES,
         "copy_fetch_kib": cf["FETCH_SIZE"],
@@ -133,14 +146,15 @@ def cmd_summarize(args):
     }
     if args.sq_dir:
         sq = read_counters(os.path.join(args.sq_dir, "**", "*counter_collection.csv"))
-        _, fs = pick(sq, FORCE_KERNELS)
+        _, fs = pick(sq, kernels)
         rec["sq"] = dict(fs)
     if args.dram_dir:
         dr = read_counters(os.path.join(args.dram_dir, "**", "*counter_collection.csv"))
-        _, fd = pick(dr, FORCE_KERNELS)
+        _, fd = pick(dr, kernels)
         _, cd = pick(dr, COPY_KERNEL_HINTS)
         rec["tcc"] = {"force": dict(fd), "copy": dict(cd)}
-    with open(args.out_json, "w") as f:
+    out_json = args.out_json or traffic_file(args.path, args.workload)
+    with open(out_json, "w") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
         f.write("\n")
     print(json.dumps(rec, indent=1, sort_keys=True))
@@ -177,10 +191,14 @@ def main():
     s.add_argument("--write-dir", required=True)
     s.add_argument("--sq-dir", default=None)
     s.add_argument("--dram-dir", default=None)
+    s.add_argument("--path", choices=("tile", "symmetric"), default="symmetric")
+    s.add_argument("--variant", type=int, required=True,
+                   help="the variant the profiled run used (printed by run)")
     s.add_argument("--workload", default="plummer1m")
     s.add_argument("--n", type=int, default=1 << 20)
     s.add_argument("--panel", type=int, default=2048)
-    s.add_argument("--out-json", required=True)
+    s.add_argument("--out-json", default=None,
+                   help="default: the record bench.py reads for this path and workload")
     t = sub.add_parser("trace-report")
     t.add_argument("--dir", required=True)
     a = ap.parse_args()
