@@ -179,6 +179,43 @@ def cmd_trace_report(args):
     print("\n".join(lines))
 
 
+def _short_kernel_name(name: str) -> str:
+    """Kernel name without namespaces and argument list, template arguments
+    kept: symmetric_task_kernel<8, 1, 4, 6, 1>."""
+    base = name.replace("(anonymous namespace)::", "").split("(")[0]
+    if base.startswith("void "):
+        base = base[5:]
+    head, sep, tmpl = base.partition("<")
+    return head.split("::")[-1] + (sep + tmpl if sep else "")
+
+
+def cmd_dispatch_report(args):
+    """Markdown table of a rocprofv3 kernel_trace.csv with one row per kernel
+    and launch shape (grid, block): dispatch count and mean / min duration.
+    The same kernel launched on different problem sizes gets separate rows."""
+    files = glob.glob(os.path.join(args.dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(args.dir)
+    groups = defaultdict(list)
+    order = []
+    with open(files[0], newline="") as f:
+        for row in csv.DictReader(f):
+            key = (_short_kernel_name(row["Kernel_Name"]), int(row["Grid_Size_X"]),
+                   int(row["Grid_Size_Y"]), int(row["Workgroup_Size_X"]))
+            if key not in groups:
+                order.append(key)
+            groups[key].append((int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e6)
+    lines = ["| kernel | grid x (threads) | grid y | block | dispatches | mean ms | min ms |",
+             "|---|---|---|---|---|---|---|"]
+    for key in order:
+        ms = groups[key]
+        if sum(ms) < args.min_total_ms:
+            continue
+        lines.append("| `%s` | %d | %d | %d | %d | %.4f | %.4f |" % (
+            key[0], key[1], key[2], key[3], len(ms), sum(ms) / len(ms), min(ms)))
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -201,8 +238,13 @@ def main():
                    help="default: the record bench.py reads for this path and workload")
     t = sub.add_parser("trace-report")
     t.add_argument("--dir", required=True)
+    d = sub.add_parser("dispatch-report")
+    d.add_argument("--dir", required=True)
+    d.add_argument("--min-total-ms", type=float, default=0.0,
+                   help="leave out (kernel, shape) groups whose total time is below this")
     a = ap.parse_args()
-    {"run": cmd_run, "summarize": cmd_summarize, "trace-report": cmd_trace_report}[a.cmd](a)
+    {"run": cmd_run, "summarize": cmd_summarize, "trace-report": cmd_trace_report,
+     "dispatch-report": cmd_dispatch_report}[a.cmd](a)
 
 
 if __name__ == "__main__":

@@ -113,6 +113,9 @@ __global__ __launch_bounds__(256) void splitj_reduce_kernel(const float4 *__rest
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
   float ax = 0.0f, ay = 0.0f, az = 0.0f;
+  // unrolled so that several chunk rows are in flight per lane (the sum is
+  // still taken in ascending chunk order)
+#pragma unroll 8
   for (int c = 0; c < n_chunks; ++c) {
     const float4 p = partial[(size_t)c * n + i];
     ax += p.x;

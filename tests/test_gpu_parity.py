@@ -27,7 +27,7 @@ def gpu_accel(pm_np, G=1.0, eps2=1e-4, variant=None):
         nb.nbody_accel_variant(pm, G, eps2, out, variant)
     torch.cuda.synchronize()
     res = out.cpu().numpy()
-    assert np.array_equal(pm.cpu().numpy(), pm_np), "posmass was modified"
+    assert np.array_equal(pm.cpu().numpy(), pm_np, equal_nan=True), "posmass was modified"
     return res
 
 
@@ -283,7 +283,7 @@ def sym_accel(pm_np, G=1.0, eps2=1e-4, variant=-1):
                      dtype=torch.uint8, device=DEV)
     nb.nbody_accel_symmetric(t, G, eps2, out, ws, variant)
     torch.cuda.synchronize()
-    assert np.array_equal(t.cpu().numpy(), pm_np), "posmass was modified"
+    assert np.array_equal(t.cpu().numpy(), pm_np, equal_nan=True), "posmass was modified"
     return out.cpu().numpy()
 
 
@@ -456,3 +456,43 @@ def test_one_massive_body_among_test_particles(path):
     expect = float(F32(G)) * M * d / ((d * d).sum(axis=1) + e)[:, None] ** 1.5
     expect[1234] = 0.0
     assert_parity(a, expect, f"test particles {path}")
+
+
+@pytest.mark.parametrize("path", sorted(PATHS))
+@pytest.mark.parametrize("bad", ["nan_x", "nan_mass"])
+def test_nan_body_propagates(path, bad):
+    """The hot path does not check its data: a body with a NaN coordinate or a
+    NaN mass turns every acceleration component into NaN (every body pairs
+    with it), the kernels still finish, and accel.w stays 0."""
+    n = 1500
+    pm, _ = workloads.uniform_cube(n, seed=62)
+    k = 777
+    if bad == "nan_x":
+        pm[k, 0] = np.nan
+    else:
+        pm[k, 3] = np.nan
+    a = PATHS[path](pm)
+    assert np.all(np.isnan(a[:, :3])), f"{path} {bad}: non-NaN at {np.argwhere(~np.isnan(a[:, :3]))[:4]}"
+    assert np.all(a[:, 3] == 0.0)
+
+
+@pytest.mark.parametrize("path", sorted(PATHS))
+def test_infinite_coordinate_body(path):
+    """A body at z = +inf: every pair with it has |r|^2 = inf, so its weight
+    rsq(inf)^3 is exactly 0.  The x and y components of the other bodies then
+    get exactly nothing from it (0 * finite), and match the oracle without
+    that body; their z components are 0 * inf = NaN, and the body's own row
+    is NaN (its self term has r_z = inf - inf)."""
+    n = 1500
+    pm, _ = workloads.uniform_cube(n, seed=62)
+    k = 777
+    pm[k, 2] = np.inf
+    a = PATHS[path](pm)
+    assert np.all(a[:, 3] == 0.0)
+    assert np.all(np.isnan(a[:, 2]))
+    assert np.all(np.isnan(a[k, :3]))
+    rest = np.delete(np.arange(n), k)
+    ref = ref_accel(np.delete(pm, k, axis=0))
+    got = a[rest].copy()
+    got[:, 2] = ref[:, 2]           # z is NaN by construction; compare x and y
+    assert_parity(got, ref, f"inf body {path}")
