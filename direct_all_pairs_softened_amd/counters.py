@@ -199,20 +199,30 @@ def cmd_dispatch_report(args):
     groups = defaultdict(list)
     order = []
     with open(files[0], newline="") as f:
-        for row in csv.DictReader(f):
-            key = (_short_kernel_name(row["Kernel_Name"]), int(row["Grid_Size_X"]),
-                   int(row["Grid_Size_Y"]), int(row["Workgroup_Size_X"]))
-            if key not in groups:
-                order.append(key)
-            groups[key].append((int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e6)
-    lines = ["| kernel | grid x (threads) | grid y | block | dispatches | mean ms | min ms |",
-             "|---|---|---|---|---|---|---|"]
+        rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+    prev = ""
+    for row in rows:
+        name = _short_kernel_name(row["Kernel_Name"])
+        key = (name, int(row["Grid_Size_X"]), int(row["Grid_Size_Y"]),
+               int(row["Workgroup_Size_X"]), prev if args.by_predecessor else "")
+        if key not in groups:
+            order.append(key)
+        groups[key].append((int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e6)
+        prev = "%s [grid y %s]" % (name.split("<")[0], row["Grid_Size_Y"])
+    head = "| kernel | grid x (threads) | grid y | block | dispatches | mean ms | median ms | min ms |"
+    rule = "|---|---|---|---|---|---|---|---|"
+    if args.by_predecessor:
+        head, rule = head + " launched after |", rule + "---|"
+    lines = [head, rule]
     for key in order:
-        ms = groups[key]
+        ms = sorted(groups[key])
         if sum(ms) < args.min_total_ms:
             continue
-        lines.append("| `%s` | %d | %d | %d | %d | %.4f | %.4f |" % (
-            key[0], key[1], key[2], key[3], len(ms), sum(ms) / len(ms), min(ms)))
+        line = "| `%s` | %d | %d | %d | %d | %.4f | %.4f | %.4f |" % (
+            key[0], key[1], key[2], key[3], len(ms), sum(ms) / len(ms), ms[len(ms) // 2], ms[0])
+        if args.by_predecessor:
+            line += " %s |" % key[4]
+        lines.append(line)
     print("\n".join(lines))
 
 
@@ -242,6 +252,9 @@ def main():
     d.add_argument("--dir", required=True)
     d.add_argument("--min-total-ms", type=float, default=0.0,
                    help="leave out (kernel, shape) groups whose total time is below this")
+    d.add_argument("--by-predecessor", action="store_true",
+                   help="also split groups by the kernel dispatched just before (tells apart "
+                        "second passes that follow first passes of different shapes)")
     a = ap.parse_args()
     {"run": cmd_run, "summarize": cmd_summarize, "trace-report": cmd_trace_report,
      "dispatch-report": cmd_dispatch_report}[a.cmd](a)
