@@ -286,6 +286,27 @@ def suite(nb, torch, names):
         torch.cuda.empty_cache()
 
 
+def suite_report(path):
+    """Markdown tables of the JSON lines written by --suite (formatting only)."""
+    recs = [json.loads(line) for line in open(path) if line.strip().startswith("{")]
+    out = ["| workload | pass | reps | median ms | min ms | 10^9 interactions/s | % of 157.3 TF |",
+           "|---|---|---|---|---|---|---|"]
+    for r in recs:
+        for name, f in r["force"].items():
+            out.append("| %s | %s | %d | %.4g | %.4g | %.0f | %.1f |" % (
+                r["workload"], name, f["reps"], f["ms_median"], f["ms_min"],
+                f["interactions_per_s_billions"], f["pct_fp32_peak"]))
+    out += ["", "| workload | steps x dt | force pass | median step ms | energy drift | "
+            "momentum change |", "|---|---|---|---|---|---|"]
+    for r in recs:
+        run = r.get("run")
+        if run:
+            out.append("| %s | %d x %g | %s | %.4g | %.2e | %.2e |" % (
+                r["workload"], run["steps"], run["dt"], run["force_pass"],
+                run["step_ms_median"], run["energy_drift"], run["momentum_change"]))
+    print("\n".join(out))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -308,7 +329,12 @@ def main():
                          "and whole KDK runs, one JSON line each, instead of the step benchmark")
     ap.add_argument("--sweep-paths", default="tile,symmetric,splitj",
                     help="comma-separated subset of tile, symmetric, splitj, range (--sweep)")
+    ap.add_argument("--suite-report", default=None, metavar="JSONL",
+                    help="print Markdown tables of a file of --suite output and exit (no GPU)")
     args = ap.parse_args()
+    if args.suite_report:
+        suite_report(args.suite_report)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
