@@ -1,8 +1,9 @@
 """Integrator and energy on the GPU: the kick/drift kernels against the
 oracle's kick/drift on identical inputs, the energy reduction against the
 oracle's energy, and whole kick-drift-kick runs of the project's workloads
-(energy drift, momentum, accelerations at the final step checked by the
-oracle on the GPU's own state, time reversibility)."""
+(energy drift, momentum, the trajectory against the oracle's own float64
+integration, force parity on the oracle's evolved state, time
+reversibility).  No oracle input is taken from a GPU result."""
 import math
 
 import numpy as np
@@ -12,7 +13,7 @@ import torch
 import direct_all_pairs_softened_amd as nb
 import oracle
 import workloads
-from parity import assert_parity, log, sample_rows
+from parity import assert_parity, errors, log
 
 pytestmark = pytest.mark.gpu
 
@@ -129,16 +130,30 @@ def test_plummer16k_ten_steps():
     drift = abs(es[-1]["E"] - es[0]["E"]) / abs(es[0]["E"])
     log(f"plummer16k energy drift {drift:.3e}")
     assert drift <= 1e-4
-    # accelerations at step 10, checked by the oracle on the GPU's own state
     pm_np = pm.cpu().numpy()
-    pos, mass = oracle.split_posmass(pm_np)
-    ref = oracle.accel(pos, mass, w.G, float(F32(w.eps2)))
-    assert_parity(acc.cpu().numpy(), ref, "plummer16k step 10")
     assert np.array_equal(pm_np[:, 3], pm0[:, 3])
     # trajectory against the oracle's own float64 integration
     pos0, mass0 = oracle.split_posmass(pm0)
-    x_ref, v_ref, _ = oracle.kdk(pos0, v0, mass0, w.G, float(F32(w.eps2)), float(F32(w.dt)),
-                                 w.steps)
+    x_ref, v_ref, a_ref = oracle.kdk(pos0, v0, mass0, w.G, float(F32(w.eps2)),
+                                     float(F32(w.dt)), w.steps)
+    # accelerations at step 10: the oracle's step-10 state, rounded to float32,
+    # is the input of both the GPU force pass and the oracle's force (no oracle
+    # input comes from the GPU run)
+    pm10 = np.concatenate([x_ref.astype(F32), pm0[:, 3:4]], axis=1)
+    t10 = to_dev(pm10)
+    a10 = torch.empty_like(t10)
+    nb.nbody_accel(t10, w.G, w.eps2, a10)
+    torch.cuda.synchronize()
+    pos10, mass10 = oracle.split_posmass(pm10)
+    assert_parity(a10.cpu().numpy(), oracle.accel(pos10, mass10, w.G, float(F32(w.eps2))),
+                  "plummer16k step-10 state")
+    # the GPU run's own step-10 accelerations against the oracle run's: the
+    # states differ by the trajectory error checked below, so only the
+    # relative L2 bar is asserted; the worst body is reported
+    l2, worst = errors(acc.cpu().numpy(), a_ref)
+    log(f"plummer16k step 10: GPU run's accel vs oracle run's accel, rel L2 {l2:.2e}, "
+        f"worst body {worst:.2e}")
+    assert l2 <= 1e-5
     # ten fp32 drifts round x ten times (~0.5 ulp each), so the bound scales
     # with |x|: untruncated Plummer bodies reach |x| ~ 10^2 where 1 ulp ~ 1e-5
     dx = np.abs(pm_np[:, :3] - x_ref)
@@ -168,8 +183,9 @@ def test_time_reversibility():
 
 def test_collision1m_twenty_steps():
     """Two Plummer spheres, N = 1000003, 20 KDK steps of dt = 1e-3:
-    momentum change <= 1e-6, relative energy drift <= 1e-3, and the final
-    accelerations of sampled bodies against the oracle."""
+    momentum change <= 1e-6, relative energy drift <= 1e-3, and Newton's third
+    law on the final accelerations (the oracle cannot integrate 10^6 bodies in
+    a test's time; step-0 parity is test_collision1m_ragged_sampled)."""
     w = workloads.WORKLOADS["collision1m"]
     pm0, v0 = workloads.make("collision1m")
     log("collision1m: integrating")
@@ -181,11 +197,13 @@ def test_collision1m_twenty_steps():
     assert dp <= 1e-6
     assert drift <= 1e-3
     pm_np = pm.cpu().numpy()
-    rows = sample_rows(w.n, 256, seed=6)
-    pos, mass = oracle.split_posmass(pm_np)
-    ref = oracle.accel_rows(pos, mass, w.G, float(F32(w.eps2)), rows)
-    assert_parity(acc.cpu().numpy()[rows], ref, "collision1m step 20")
     assert np.array_equal(pm_np[:, 3], pm0[:, 3])
+    a = acc.cpu().numpy()[:, :3].astype(np.float64)
+    m = pm_np[:, 3:4].astype(np.float64)
+    newton = np.linalg.norm((m * a).sum(axis=0)) / (m[:, 0] * np.linalg.norm(a, axis=1)).sum()
+    log(f"collision1m step 20: |sum m a| / sum m|a| = {newton:.2e}")
+    assert newton <= 1e-6
+    assert np.all(a[:, :3] == a[:, :3])          # no NaN
 
 
 # ---------------------------------------------------------------------------
