@@ -165,7 +165,7 @@ def sweep(nb, torch, w, pm, acc, reps, paths):
         del ws
 
 
-# timed force passes per workload in --suite (the benchmark spec's per-config reps)
+# timed force passes per workload in --suite (repetitions per workload)
 SUITE_REPS = {"uniform1k": 100, "plummer16k": 100, "lognormal128k": 50, "plummer1m": 10,
               "collision1m": 5}
 
@@ -337,7 +337,7 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
               "(the force pass would shard by i with an all-gather of positions).",
               file=sys.stderr)
         sys.exit(2)
