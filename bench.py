@@ -205,6 +205,14 @@ def suite(nb, torch, names):
         force[f"symmetric_v{sv}"] = _stats(
             w, _time(torch, lambda: nb.nbody_accel_symmetric(pm, w.G, w.eps2, acc, sym_ws, sv),
                      reps))
+        if w.n >= 100000:
+            pv = nb.nbody_accel_symmetric_potential_variant_for_n(w.n)
+            pot_ws = torch.empty(nb.nbody_accel_symmetric_potential_workspace_bytes(w.n, pv),
+                                 dtype=torch.uint8, device=dev)
+            force[f"symmetric_potential_v{pv}"] = _stats(
+                w, _time(torch, lambda: nb.nbody_accel_symmetric_potential(
+                    pm, w.G, w.eps2, acc, pot_ws, pv), reps))
+            del pot_ws
         if name == "plummer1m":
             # the same one-sided arithmetic over 96-bit float3 records and SoA
             pos3 = pm[:, :3].contiguous()
@@ -429,6 +437,24 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     energy_ms = e0.elapsed_time(e1)
+    checkpoint_ms = None
+    if args.path == "symmetric":
+        # a checkpoint step's force pass with the potentials in accel.w, then
+        # the O(N) energy from them (in place of force pass + energy pass)
+        pv = nb.nbody_accel_symmetric_potential_variant_for_n(w.n)
+        pot_ws = torch.empty(nb.nbody_accel_symmetric_potential_workspace_bytes(w.n, pv),
+                             dtype=torch.uint8, device=dev)
+        pws = torch.empty(nb.nbody_energy_from_potential_workspace_bytes(w.n),
+                          dtype=torch.uint8, device=dev)
+        acc_pot = torch.empty_like(acc)
+        nb.nbody_accel_symmetric_potential(pm, w.G, w.eps2, acc_pot, pot_ws, pv)
+        e0.record(stream)
+        nb.nbody_accel_symmetric_potential(pm, w.G, w.eps2, acc_pot, pot_ws, pv)
+        nb.nbody_energy_from_potential(pm, vel, acc_pot, pws, stats)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        checkpoint_ms = e0.elapsed_time(e1)
+        del pot_ws, pws, acc_pot
 
     traffic = traffic_per_launch(args.path, variant, w.name)
     out = {
@@ -458,6 +484,7 @@ def main():
         "pct_fp32_peak": 100.0 * achieved / PEAK_FP32_TFLOPS,
         "force_ms": force_avg,
         "energy_ms": energy_ms,
+        "checkpoint_force_energy_ms": checkpoint_ms,
         "roofline": {
             "bound": "alu",
             "achieved": achieved,

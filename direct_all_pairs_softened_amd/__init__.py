@@ -40,6 +40,9 @@ EXPORTS = (
     "nbody_accel_symmetric", "nbody_accel_symmetric_workspace_bytes",
     "nbody_accel_symmetric_variant_count", "nbody_accel_symmetric_panel",
     "nbody_accel_symmetric_variant_for_n",
+    "nbody_accel_symmetric_potential", "nbody_accel_symmetric_potential_workspace_bytes",
+    "nbody_accel_symmetric_potential_variant_count", "nbody_accel_symmetric_potential_panel",
+    "nbody_accel_symmetric_potential_variant_for_n",
     "nbody_accel_f3aos", "nbody_accel_soa",
     "nbody_leapfrog_step", "nbody_kick",
     "nbody_energy", "nbody_energy_workspace_bytes",
@@ -93,6 +96,12 @@ def load_library(path: str | None = None):
         "nbody_accel_symmetric_variant_count": (c_int, []),
         "nbody_accel_symmetric_panel": (c_int, [c_int]),
         "nbody_accel_symmetric_variant_for_n": (c_int, [c_i64]),
+        "nbody_accel_symmetric_potential": (c_int, [vp, c_i64, c_f, c_f, vp, c_int, vp, c_sz,
+                                                    vp]),
+        "nbody_accel_symmetric_potential_workspace_bytes": (c_sz, [c_i64, c_int]),
+        "nbody_accel_symmetric_potential_variant_count": (c_int, []),
+        "nbody_accel_symmetric_potential_panel": (c_int, [c_int]),
+        "nbody_accel_symmetric_potential_variant_for_n": (c_int, [c_i64]),
         "nbody_accel_f3aos": (c_int, [vp, vp, c_i64, c_f, c_f, vp, vp]),
         "nbody_accel_soa": (c_int, [vp, vp, vp, vp, c_i64, c_f, c_f, vp, vp, vp, vp]),
         "nbody_leapfrog_step": (c_int, [vp, vp, vp, c_f, c_i64, vp]),
@@ -306,6 +315,38 @@ def nbody_accel_symmetric(posmass, G: float, eps2: float, accel_out, workspace,
                                                 _f32(accel_out, "accel_out", (4,)),
                                                 int(variant), ws, nbytes, _stream(stream)),
            "nbody_accel_symmetric")
+
+
+def nbody_accel_symmetric_potential_workspace_bytes(n: int, variant: int = -1) -> int:
+    return int(load_library().nbody_accel_symmetric_potential_workspace_bytes(int(n),
+                                                                              int(variant)))
+
+
+def nbody_accel_symmetric_potential_variant_count() -> int:
+    return int(load_library().nbody_accel_symmetric_potential_variant_count())
+
+
+def nbody_accel_symmetric_potential_panel(variant: int) -> int:
+    return int(load_library().nbody_accel_symmetric_potential_panel(int(variant)))
+
+
+def nbody_accel_symmetric_potential_variant_for_n(n: int) -> int:
+    return int(load_library().nbody_accel_symmetric_potential_variant_for_n(int(n)))
+
+
+def nbody_accel_symmetric_potential(posmass, G: float, eps2: float, accel_out, workspace,
+                                    variant: int = -1, stream=None):
+    """Pair-symmetric force pass with Phi_i in accel_out[:, 3]; workspace: a GPU
+    tensor of at least nbody_accel_symmetric_potential_workspace_bytes(N, variant)
+    bytes."""
+    n = _n_of(posmass)
+    if _n_of(accel_out) != n:
+        raise ValueError("accel_out must have N rows")
+    ws = _dev(workspace, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load_library().nbody_accel_symmetric_potential(
+        _f32(posmass, "posmass", (4,)), n, G, eps2, _f32(accel_out, "accel_out", (4,)),
+        int(variant), ws, nbytes, _stream(stream)), "nbody_accel_symmetric_potential")
 
 
 def nbody_accel_f3aos(pos, mass, G: float, eps2: float, accel_out, stream=None):

@@ -236,46 +236,85 @@ int nbody_accel_splitj_tree(const float *posmass, int64_t n, float G, float eps2
                                               terms, workspace, as_stream(stream)));
 }
 
-static int sym_variant(int v, int64_t n) { return v < 0 ? nbody::symmetric_variant_for_n(n) : v; }
-
-int nbody_accel_symmetric_variant_count(void) { return nbody::symmetric_variant_count(); }
-
-int nbody_accel_symmetric_variant_for_n(int64_t n) { return nbody::symmetric_variant_for_n(n); }
-
-int nbody_accel_symmetric_panel(int variant) {
-  if (variant < 0) return NBODY_ERR_INVALID_ARG;
-  const int v = variant;
-  if (v >= nbody::symmetric_variant_count()) return NBODY_ERR_INVALID_ARG;
-  return nbody::symmetric_panel(v);
+static int sym_variant(int v, int64_t n, bool pot) {
+  return v < 0 ? nbody::symmetric_variant_for_n(n, pot) : v;
 }
 
-size_t nbody_accel_symmetric_workspace_bytes(int64_t n, int variant) {
-  const int v = sym_variant(variant, n);
-  if (!n_ok(n) || v >= nbody::symmetric_variant_count()) return 0;
-  return nbody::symmetric_workspace_bytes(n, v);
+static size_t sym_workspace_bytes(int64_t n, int variant, bool pot) {
+  const int v = sym_variant(variant, n, pot);
+  if (!n_ok(n) || v >= nbody::symmetric_variant_count(pot)) return 0;
+  return nbody::symmetric_workspace_bytes(n, v, pot);
 }
 
-int nbody_accel_symmetric(const float *posmass, int64_t n, float G, float eps2,
-                          float *accel_out, int variant, void *workspace,
-                          size_t workspace_bytes, void *stream) {
-  const int v = sym_variant(variant, n);
+static int sym_pass(const float *posmass, int64_t n, float G, float eps2, float *accel_out,
+                    int variant, bool pot, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+  const int v = sym_variant(variant, n, pot);
   if (!n_ok(n)) return NBODY_ERR_INVALID_ARG;
   if (int s = check_consts(G, eps2)) return s;
-  if (v >= nbody::symmetric_variant_count()) return NBODY_ERR_INVALID_ARG;
+  if (v >= nbody::symmetric_variant_count(pot)) return NBODY_ERR_INVALID_ARG;
   if (n == 0) return NBODY_OK;
-  const int64_t P = nbody::symmetric_panels(n, v);
+  const int64_t P = nbody::symmetric_panels(n, v, pot);
   if (P * (P + 1) / 2 > INT32_MAX) return NBODY_ERR_INVALID_ARG;
   if (!posmass || !accel_out) return NBODY_ERR_INVALID_ARG;
   if (!aligned(posmass, 16) || !aligned(accel_out, 16)) return NBODY_ERR_ALIGNMENT;
-  const size_t need = nbody::symmetric_workspace_bytes(n, v);
+  const size_t need = nbody::symmetric_workspace_bytes(n, v, pot);
   if (!workspace || workspace_bytes < need) return NBODY_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return NBODY_ERR_ALIGNMENT;
   const size_t bytes = (size_t)n * 16;
   if (overlap(posmass, bytes, accel_out, bytes) || overlap(workspace, need, posmass, bytes) ||
       overlap(workspace, need, accel_out, bytes))
     return NBODY_ERR_ALIAS;
-  return hip_status(nbody::launch_symmetric(posmass, (int)n, G, eps2, accel_out, v, workspace,
-                                            as_stream(stream)));
+  return hip_status(nbody::launch_symmetric(posmass, (int)n, G, eps2, accel_out, v, pot,
+                                            workspace, as_stream(stream)));
+}
+
+int nbody_accel_symmetric_variant_count(void) { return nbody::symmetric_variant_count(false); }
+
+int nbody_accel_symmetric_variant_for_n(int64_t n) {
+  return nbody::symmetric_variant_for_n(n, false);
+}
+
+int nbody_accel_symmetric_panel(int variant) {
+  if (variant < 0 || variant >= nbody::symmetric_variant_count(false))
+    return NBODY_ERR_INVALID_ARG;
+  return nbody::symmetric_panel(variant, false);
+}
+
+size_t nbody_accel_symmetric_workspace_bytes(int64_t n, int variant) {
+  return sym_workspace_bytes(n, variant, false);
+}
+
+int nbody_accel_symmetric(const float *posmass, int64_t n, float G, float eps2,
+                          float *accel_out, int variant, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  return sym_pass(posmass, n, G, eps2, accel_out, variant, false, workspace, workspace_bytes,
+                  stream);
+}
+
+int nbody_accel_symmetric_potential_variant_count(void) {
+  return nbody::symmetric_variant_count(true);
+}
+
+int nbody_accel_symmetric_potential_variant_for_n(int64_t n) {
+  return nbody::symmetric_variant_for_n(n, true);
+}
+
+int nbody_accel_symmetric_potential_panel(int variant) {
+  if (variant < 0 || variant >= nbody::symmetric_variant_count(true))
+    return NBODY_ERR_INVALID_ARG;
+  return nbody::symmetric_panel(variant, true);
+}
+
+size_t nbody_accel_symmetric_potential_workspace_bytes(int64_t n, int variant) {
+  return sym_workspace_bytes(n, variant, true);
+}
+
+int nbody_accel_symmetric_potential(const float *posmass, int64_t n, float G, float eps2,
+                                    float *accel_out, int variant, void *workspace,
+                                    size_t workspace_bytes, void *stream) {
+  return sym_pass(posmass, n, G, eps2, accel_out, variant, true, workspace, workspace_bytes,
+                  stream);
 }
 
 int nbody_leapfrog_step(float *posmass, float *vel, const float *accel, float dt, int64_t n,

@@ -59,14 +59,16 @@ size_t splitj_tree_workspace_bytes(int64_t n, int64_t j_chunk, int terms);
 hipError_t launch_splitj_tree(const float *posmass, int n, float G, float eps2, float *accel,
                               int j_chunk, int terms, void *workspace, hipStream_t stream);
 
-// Pair-symmetric force pass (each pair once, applied to both bodies).
-int symmetric_variant_count();
-int symmetric_variant_for_n(int64_t n);
-int symmetric_panel(int v);
-int64_t symmetric_panels(int64_t n, int v);
-size_t symmetric_workspace_bytes(int64_t n, int v);
+// Pair-symmetric force pass (each pair once, applied to both bodies).  pot
+// selects the variants that also store Phi_i = -G sum_{j != i} m_j /
+// sqrt(r^2 + eps^2) in accel.w; their variant ids are a table of their own.
+int symmetric_variant_count(bool pot);
+int symmetric_variant_for_n(int64_t n, bool pot);
+int symmetric_panel(int v, bool pot);
+int64_t symmetric_panels(int64_t n, int v, bool pot);
+size_t symmetric_workspace_bytes(int64_t n, int v, bool pot);
 hipError_t launch_symmetric(const float *posmass, int n, float G, float eps2, float *accel,
-                            int v, void *workspace, hipStream_t stream);
+                            int v, bool pot, void *workspace, hipStream_t stream);
 
 // Integrator.
 hipError_t launch_leapfrog(float *posmass, float *vel, const float *accel, float dt, int n,

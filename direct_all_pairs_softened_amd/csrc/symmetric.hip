@@ -41,16 +41,18 @@ namespace {
 // differences, then all d^2, all rsq, ...), which gives each wave IL
 // independent chains to issue from; IL = 1 is one pair after the other.  The
 // arithmetic of each pair, and its order of accumulation, do not depend on IL.
-template <int K, int IL>
+// POT adds the potential sums: i gains m_j inv, j gains m_i inv (two more
+// multiply-adds per pair; the force arithmetic is unchanged).
+template <int K, int IL, bool POT>
 __device__ __forceinline__ void sym_step(const float (&xi)[K], const float (&yi)[K],
                                          const float (&zi)[K], const float (&mi)[K], float xj,
                                          float yj, float zj, float mj, float eps2, float (&ax)[K],
-                                         float (&ay)[K], float (&az)[K], float &cx, float &cy,
-                                         float &cz) {
+                                         float (&ay)[K], float (&az)[K], float (&ap)[K],
+                                         float &cx, float &cy, float &cz, float &cp) {
   static_assert(K % IL == 0, "interleave width must divide K");
 #pragma unroll
   for (int h = 0; h < K; h += IL) {
-    float dx[IL], dy[IL], dz[IL], w[IL];
+    float dx[IL], dy[IL], dz[IL], inv[IL], w[IL];
 #pragma unroll
     for (int q = 0; q < IL; ++q) {
       dx[q] = xj - xi[h + q];
@@ -64,15 +66,16 @@ __device__ __forceinline__ void sym_step(const float (&xi)[K], const float (&yi)
 #pragma unroll
     for (int q = 0; q < IL; ++q) w[q] = __builtin_fmaf(dz[q], dz[q], w[q]);
 #pragma unroll
-    for (int q = 0; q < IL; ++q) w[q] = __builtin_amdgcn_rsqf(w[q]);
+    for (int q = 0; q < IL; ++q) inv[q] = __builtin_amdgcn_rsqf(w[q]);
 #pragma unroll
-    for (int q = 0; q < IL; ++q) w[q] = (w[q] * w[q]) * w[q];
+    for (int q = 0; q < IL; ++q) w[q] = (inv[q] * inv[q]) * inv[q];
 #pragma unroll
     for (int q = 0; q < IL; ++q) {
       const float sj = mj * w[q];
       ax[h + q] = __builtin_fmaf(sj, dx[q], ax[h + q]);
       ay[h + q] = __builtin_fmaf(sj, dy[q], ay[h + q]);
       az[h + q] = __builtin_fmaf(sj, dz[q], az[h + q]);
+      if constexpr (POT) ap[h + q] = __builtin_fmaf(mj, inv[q], ap[h + q]);
     }
 #pragma unroll
     for (int q = 0; q < IL; ++q) {
@@ -80,22 +83,31 @@ __device__ __forceinline__ void sym_step(const float (&xi)[K], const float (&yi)
       cx = __builtin_fmaf(si, dx[q], cx);
       cy = __builtin_fmaf(si, dy[q], cy);
       cz = __builtin_fmaf(si, dz[q], cz);
+      if constexpr (POT) cp = __builtin_fmaf(mi[h + q], inv[q], cp);
     }
   }
 }
 
-template <int K, int KP, int W, int IL, bool DIAG>
+// Sums kept per body: the three acceleration components, plus the potential
+// sum with POT.
+template <bool POT>
+constexpr int sym_sums() {
+  return POT ? 4 : 3;
+}
+
+template <int K, int KP, int W, int IL, bool POT, bool DIAG>
 __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, int I, int J,
                                          int P, float eps2, float *__restrict__ part,
-                                         float (*csum)[KP][3][kWave]) {
+                                         float (*csum)[KP][sym_sums<POT>()][kWave]) {
   constexpr int B = W * kWave * K;
   constexpr int JG = kWave * KP;
   constexpr int NG = B / JG;
+  constexpr int NC = sym_sums<POT>();
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
 
-  float xi[K], yi[K], zi[K], mi[K], ax[K], ay[K], az[K];
+  float xi[K], yi[K], zi[K], mi[K], ax[K], ay[K], az[K], ap[K];
 #pragma unroll
   for (int q = 0; q < K; ++q) {
     const int i = I * B + wave * (kWave * K) + q * kWave + lane;
@@ -107,10 +119,11 @@ __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, i
     ax[q] = 0.0f;
     ay[q] = 0.0f;
     az[q] = 0.0f;
+    ap[q] = 0.0f;
   }
 
   for (int g = 0; g < NG; ++g) {
-    float xj[KP], yj[KP], zj[KP], mj[KP], cx[KP], cy[KP], cz[KP];
+    float xj[KP], yj[KP], zj[KP], mj[KP], cx[KP], cy[KP], cz[KP], cp[KP];
 #pragma unroll
     for (int p = 0; p < KP; ++p) {
       const int j = J * B + g * JG + p * kWave + lane;
@@ -122,13 +135,14 @@ __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, i
       cx[p] = 0.0f;
       cy[p] = 0.0f;
       cz[p] = 0.0f;
+      cp[p] = 0.0f;
     }
     for (int s = 0; s < kWave; ++s) {
 #pragma unroll
       for (int p = 0; p < KP; ++p) {
         if constexpr (!DIAG) {
-          sym_step<K, IL>(xi, yi, zi, mi, xj[p], yj[p], zj[p], mj[p], eps2, ax, ay, az, cx[p],
-                          cy[p], cz[p]);
+          sym_step<K, IL, POT>(xi, yi, zi, mi, xj[p], yj[p], zj[p], mj[p], eps2, ax, ay, az, ap,
+                               cx[p], cy[p], cz[p], cp[p]);
         } else {
 #pragma unroll
         for (int q = 0; q < K; ++q) {
@@ -143,6 +157,12 @@ __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, i
           ax[q] = __builtin_fmaf(sj, dx, ax[q]);
           ay[q] = __builtin_fmaf(sj, dy, ay[q]);
           az[q] = __builtin_fmaf(sj, dz, az[q]);
+          if constexpr (POT) {
+            // lane l meets its own body at step 0 of the sweep whose j-bodies
+            // are that body's group: the self term m_i / eps is left out
+            const bool self = s == 0 && g * KP + p == wave * K + q;
+            ap[q] = __builtin_fmaf(self ? 0.0f : mj[p], inv, ap[q]);
+          }
         }
         }
         xj[p] = rotate_lanes(xj[p]);
@@ -153,6 +173,7 @@ __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, i
           cx[p] = rotate_lanes(cx[p]);
           cy[p] = rotate_lanes(cy[p]);
           cz[p] = rotate_lanes(cz[p]);
+          if constexpr (POT) cp[p] = rotate_lanes(cp[p]);
         }
       }
     }
@@ -163,14 +184,16 @@ __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, i
         csum[wave][p][0][lane] = cx[p];
         csum[wave][p][1][lane] = cy[p];
         csum[wave][p][2][lane] = cz[p];
+        if constexpr (POT) csum[wave][p][3][lane] = cp[p];
       }
       __syncthreads();
-      for (int e = tid; e < KP * 3 * kWave; e += W * kWave) {
-        const int p = e / (3 * kWave), c = (e / kWave) % 3, l = e % kWave;
+      for (int e = tid; e < KP * NC * kWave; e += W * kWave) {
+        const int p = e / (NC * kWave), c = (e / kWave) % NC, l = e % kWave;
         float sum = 0.0f;
 #pragma unroll
         for (int w = 0; w < W; ++w) sum += csum[w][p][c][l];
-        part[(((size_t)J * P + I) * 3 + c) * B + g * JG + p * kWave + l] = -sum;
+        // the force on j from i points the other way; the potential does not
+        part[(((size_t)J * P + I) * NC + c) * B + g * JG + p * kWave + l] = c < 3 ? -sum : sum;
       }
       __syncthreads();
     }
@@ -179,41 +202,47 @@ __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, i
 #pragma unroll
   for (int q = 0; q < K; ++q) {
     const int b = wave * (kWave * K) + q * kWave + lane;
-    float *row = part + ((size_t)I * P + J) * 3 * B + b;
+    float *row = part + ((size_t)I * P + J) * NC * B + b;
     row[0] = ax[q];
     row[B] = ay[q];
     row[2 * B] = az[q];
+    if constexpr (POT) row[3 * B] = ap[q];
   }
 }
 
 // One block per task; blockIdx.x = J (J + 1) / 2 + I enumerates I <= J.
-template <int K, int KP, int W, int OCC, int IL>
+template <int K, int KP, int W, int OCC, int IL, bool POT>
 __global__ __launch_bounds__(W *kWave) __attribute__((amdgpu_waves_per_eu(OCC))) void
 symmetric_task_kernel(const float4 *__restrict__ pm, int n, int P, float eps2,
                       float *__restrict__ part) {
-  __shared__ float csum[W][KP][3][kWave];
+  __shared__ float csum[W][KP][sym_sums<POT>()][kWave];
   int Ic, Jc;
   decode_panel_pair(blockIdx.x, Ic, Jc);
   if (Ic == Jc)
-    sym_task<K, KP, W, IL, true>(pm, n, Ic, Jc, P, eps2, part, csum);
+    sym_task<K, KP, W, IL, POT, true>(pm, n, Ic, Jc, P, eps2, part, csum);
   else
-    sym_task<K, KP, W, IL, false>(pm, n, Ic, Jc, P, eps2, part, csum);
+    sym_task<K, KP, W, IL, POT, false>(pm, n, Ic, Jc, P, eps2, part, csum);
 }
 
+// a_i = G sum_J part[I][J][c][b] over J ascending; with POT the fourth sum is
+// phi_i and the output's w is Phi_i = -G phi_i, else w = 0.
+template <bool POT>
 __global__ __launch_bounds__(256) void symmetric_reduce_kernel(const float *__restrict__ part,
                                                                int n, int P, int B, float G,
                                                                float4 *__restrict__ out) {
+  constexpr int NC = sym_sums<POT>();
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
   const int I = i / B, b = i % B;
-  const float *s = part + (size_t)I * P * 3 * B + b;
-  float sx = 0.0f, sy = 0.0f, sz = 0.0f;
-  for (int J = 0; J < P; ++J, s += (size_t)3 * B) {
+  const float *s = part + (size_t)I * P * NC * B + b;
+  float sx = 0.0f, sy = 0.0f, sz = 0.0f, sp = 0.0f;
+  for (int J = 0; J < P; ++J, s += (size_t)NC * B) {
     sx += s[0];
     sy += s[B];
     sz += s[2 * B];
+    if constexpr (POT) sp += s[3 * B];
   }
-  out[i] = make_float4(G * sx, G * sy, G * sz, 0.0f);
+  out[i] = make_float4(G * sx, G * sy, G * sz, POT ? -G * sp : 0.0f);
 }
 
 // (id, K, KP, waves, occupancy target, interleave width); panel B =
@@ -236,6 +265,14 @@ __global__ __launch_bounds__(256) void symmetric_reduce_kernel(const float *__re
   X(12, 8, 1, 4, 6, 4)        \
   X(13, 8, 1, 4, 6, 2)
 
+// Variants of the pass that also sums the potential (id, K, KP, waves,
+// occupancy target); the ids are their own (nbody_accel_symmetric_potential).
+#define NBODY_SYM_POT_VARIANTS(X) \
+  X(0, 8, 1, 2, 4)                \
+  X(1, 8, 1, 4, 5)                \
+  X(2, 6, 1, 4, 6)                \
+  X(3, 8, 1, 4, 4)
+
 struct SymVariant {
   int K, KP, W;
 };
@@ -246,52 +283,89 @@ const SymVariant kSym[] = {
 #undef X
 };
 
+const SymVariant kSymPot[] = {
+#define X(id, K, KP, W, OCC) {K, KP, W},
+    NBODY_SYM_POT_VARIANTS(X)
+#undef X
+};
+
+const SymVariant &sym_table(int v, bool pot) { return pot ? kSymPot[v] : kSym[v]; }
+
 }  // namespace
 
-int symmetric_variant_count() { return (int)(sizeof(kSym) / sizeof(kSym[0])); }
+int symmetric_variant_count(bool pot) {
+  return pot ? (int)(sizeof(kSymPot) / sizeof(kSymPot[0])) : (int)(sizeof(kSym) / sizeof(kSym[0]));
+}
 
 // Measured on MI355X (force-pass sweeps): 8 i-bodies and 1 j-body per lane
 // in 4-wave blocks is fastest at 1e5-1e6 bodies; 1024-body panels (2-wave
 // blocks) give more panel pairs at the low end, 2048-body panels halve the
 // workspace at the high end.  Below ~5e4 bodies there are too few panel pairs
-// to fill the chip and the one-sided nbody_accel is faster.
-int symmetric_variant_for_n(int64_t n) { return n <= 300000 ? 8 : 9; }
+// to fill the chip and the one-sided nbody_accel is faster.  The potential
+// variants follow the same split by n.
+int symmetric_variant_for_n(int64_t n, bool pot) {
+  if (pot) return n <= 300000 ? 0 : 1;
+  return n <= 300000 ? 8 : 9;
+}
 
-int symmetric_panel(int v) { return kWave * kSym[v].W * kSym[v].K; }
+int symmetric_panel(int v, bool pot) {
+  const SymVariant &t = sym_table(v, pot);
+  return kWave * t.W * t.K;
+}
 
-int64_t symmetric_panels(int64_t n, int v) {
-  const int64_t B = symmetric_panel(v);
+int64_t symmetric_panels(int64_t n, int v, bool pot) {
+  const int64_t B = symmetric_panel(v, pot);
   return (n + B - 1) / B;
 }
 
-size_t symmetric_workspace_bytes(int64_t n, int v) {
-  if (n <= 0 || v < 0 || v >= symmetric_variant_count()) return 0;
-  const int64_t B = symmetric_panel(v), P = symmetric_panels(n, v);
-  return (size_t)P * (size_t)P * 3 * (size_t)B * sizeof(float);
+size_t symmetric_workspace_bytes(int64_t n, int v, bool pot) {
+  if (n <= 0 || v < 0 || v >= symmetric_variant_count(pot)) return 0;
+  const int64_t B = symmetric_panel(v, pot), P = symmetric_panels(n, v, pot);
+  return (size_t)P * (size_t)P * (pot ? 4 : 3) * (size_t)B * sizeof(float);
 }
 
 hipError_t launch_symmetric(const float *posmass, int n, float G, float eps2, float *accel,
-                            int v, void *workspace, hipStream_t stream) {
-  const int B = symmetric_panel(v);
-  const int P = (int)symmetric_panels(n, v);
+                            int v, bool pot, void *workspace, hipStream_t stream) {
+  const int B = symmetric_panel(v, pot);
+  const int P = (int)symmetric_panels(n, v, pot);
   const long long tasks = (long long)P * (P + 1) / 2;
   float *part = reinterpret_cast<float *>(workspace);
   const float4 *pm = reinterpret_cast<const float4 *>(posmass);
-  switch (v) {
-#define X(id, K, KP, W, OCC, IL)                                                          \
-  case id:                                                                                \
-    hipLaunchKernelGGL((symmetric_task_kernel<K, KP, W, OCC, IL>), dim3((unsigned)tasks), \
-                       dim3(W * kWave), 0, stream, pm, n, P, eps2, part);                 \
+  if (!pot) {
+    switch (v) {
+#define X(id, K, KP, W, OCC, IL)                                                       \
+  case id:                                                                             \
+    hipLaunchKernelGGL((symmetric_task_kernel<K, KP, W, OCC, IL, false>),              \
+                       dim3((unsigned)tasks), dim3(W * kWave), 0, stream, pm, n, P, eps2, \
+                       part);                                                          \
     break;
-    NBODY_SYM_VARIANTS(X)
+      NBODY_SYM_VARIANTS(X)
 #undef X
-    default:
-      return hipErrorInvalidValue;
+      default:
+        return hipErrorInvalidValue;
+    }
+  } else {
+    switch (v) {
+#define X(id, K, KP, W, OCC)                                                           \
+  case id:                                                                             \
+    hipLaunchKernelGGL((symmetric_task_kernel<K, KP, W, OCC, 1, true>),                \
+                       dim3((unsigned)tasks), dim3(W * kWave), 0, stream, pm, n, P, eps2, \
+                       part);                                                          \
+    break;
+      NBODY_SYM_POT_VARIANTS(X)
+#undef X
+      default:
+        return hipErrorInvalidValue;
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(symmetric_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, part,
-                     n, P, B, G, reinterpret_cast<float4 *>(accel));
+  if (pot)
+    hipLaunchKernelGGL(symmetric_reduce_kernel<true>, dim3((n + 255) / 256), dim3(256), 0, stream,
+                       part, n, P, B, G, reinterpret_cast<float4 *>(accel));
+  else
+    hipLaunchKernelGGL(symmetric_reduce_kernel<false>, dim3((n + 255) / 256), dim3(256), 0,
+                       stream, part, n, P, B, G, reinterpret_cast<float4 *>(accel));
   return hipGetLastError();
 }
 

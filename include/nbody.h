@@ -217,6 +217,34 @@ int nbody_accel_symmetric_panel(int variant);
 /* The variant nbody_accel_symmetric uses for n when passed -1. */
 int nbody_accel_symmetric_variant_for_n(int64_t n);
 
+/* The pair-symmetric pass that also carries each body's potential, as
+ * nbody_accel_potential does for the one-sided pass (the CAL IL loop of "CAL
+ * programming (4)" keeps the same sum, m_j times its rsq result, in the w
+ * lane of its accumulator):
+ *   accel_out[i] = (ax, ay, az, Phi_i),
+ *   Phi_i = -G sum_{j != i} m_j / sqrt(|x_j - x_i|^2 + eps^2).
+ * Each unordered pair adds m_j inv to body i's sum and m_i inv to body j's
+ * (two more multiply-adds per pair); the j = i pair is left out by an index
+ * test inside the diagonal panel pairs.  The potential sums follow the
+ * acceleration's order (per panel pair, then panel pairs in ascending
+ * order).  Its variants are a table of their own (ids below).  The xyz
+ * outputs are bitwise equal to nbody_accel_symmetric's for a variant of the
+ * same panel shape; the default choices (variant -1 on both) have the same
+ * shape at every n.  With
+ * nbody_energy_from_potential this gives the energy of a checkpoint step
+ * without a separate pair pass.
+ *   workspace  >= nbody_accel_symmetric_potential_workspace_bytes(n, variant)
+ *              bytes (16 n^2 / panel bytes), 16-byte aligned, disjoint from
+ *              posmass and accel_out; contents on return are unspecified.
+ * Other arguments and errors as nbody_accel_symmetric. */
+int nbody_accel_symmetric_potential(const float *posmass, int64_t n, float G, float eps2,
+                                    float *accel_out, int variant, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+size_t nbody_accel_symmetric_potential_workspace_bytes(int64_t n, int variant);
+int nbody_accel_symmetric_potential_variant_count(void);
+int nbody_accel_symmetric_potential_panel(int variant);
+int nbody_accel_symmetric_potential_variant_for_n(int64_t n);
+
 /* The force pass on other body layouts; same arithmetic and order as
  * nbody_accel for the same n, so the outputs are bitwise equal to its
  * (ax, ay, az).  README section 3.5 compares float4 against 12-byte float3
@@ -266,8 +294,8 @@ int nbody_energy(const float *posmass, const float *vel, int64_t n, float G,
 
 size_t nbody_energy_workspace_bytes(int64_t n);
 
-/* Energy and momentum in O(n) from the potentials nbody_accel_potential
- * stored in accel_pot[i].w: stats_out = {K, W, K + W, Px, Py, Pz, M, 0}
+/* Energy and momentum in O(n) from the potentials nbody_accel_potential or
+ * nbody_accel_symmetric_potential stored in accel_pot[i].w: stats_out = {K, W, K + W, Px, Py, Pz, M, 0}
  * with W = sum_i m_i Phi_i / 2 (each pair once).  fp64 fixed-order
  * reduction as in nbody_energy.
  *   workspace  >= nbody_energy_from_potential_workspace_bytes(n) bytes,

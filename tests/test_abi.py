@@ -233,6 +233,40 @@ def test_symmetric_host_side(lib):
     assert f(vp(A), nb.NBODY_MAX_N, 1.0, 1e-4, vp(B), 0, vp(C), 1 << 62, None) == nb.NBODY_ERR_INVALID_ARG
 
 
+def test_symmetric_potential_host_side(lib):
+    count = nb.nbody_accel_symmetric_potential_variant_count()
+    assert count >= 1
+    for v in range(count):
+        panel = nb.nbody_accel_symmetric_potential_panel(v)
+        assert panel > 0 and panel % 64 == 0
+        P = -(-1000 // panel)
+        assert nb.nbody_accel_symmetric_potential_workspace_bytes(1000, v) == P * P * 4 * panel * 4
+    for n in (1, 1000, 1 << 20):
+        assert 0 <= nb.nbody_accel_symmetric_potential_variant_for_n(n) < count
+    assert nb.nbody_accel_symmetric_potential_panel(count) == nb.NBODY_ERR_INVALID_ARG
+    assert nb.nbody_accel_symmetric_potential_panel(-1) == nb.NBODY_ERR_INVALID_ARG
+    assert nb.nbody_accel_symmetric_potential_workspace_bytes(0, 0) == 0
+    assert nb.nbody_accel_symmetric_potential_workspace_bytes(1000, count) == 0
+    assert (nb.nbody_accel_symmetric_potential_workspace_bytes(1000, -1)
+            == nb.nbody_accel_symmetric_potential_workspace_bytes(
+                1000, nb.nbody_accel_symmetric_potential_variant_for_n(1000)))
+    f = lib.nbody_accel_symmetric_potential
+    need = nb.nbody_accel_symmetric_potential_workspace_bytes(1000, 0)
+    # the plain pass's workspace is too small for the potential pass
+    assert nb.nbody_accel_symmetric_workspace_bytes(1000, 8) < need
+    assert f(vp(A), 0, 1.0, 1e-4, vp(B), 0, None, 0, None) == nb.NBODY_OK
+    assert f(vp(A), 1000, 1.0, 1e-4, vp(B), count, vp(C), need, None) == nb.NBODY_ERR_INVALID_ARG
+    assert f(vp(A), 1000, float("nan"), 1e-4, vp(B), 0, vp(C), need, None) == nb.NBODY_ERR_INVALID_ARG
+    assert f(vp(A), 1000, 1.0, -1e-4, vp(B), 0, vp(C), need, None) == nb.NBODY_ERR_INVALID_ARG
+    assert f(None, 1000, 1.0, 1e-4, vp(B), 0, vp(C), need, None) == nb.NBODY_ERR_INVALID_ARG
+    assert f(vp(A), 1000, 1.0, 1e-4, vp(B), 0, vp(C), need - 4, None) == nb.NBODY_ERR_WORKSPACE
+    assert f(vp(A), 1000, 1.0, 1e-4, vp(B), 0, None, need, None) == nb.NBODY_ERR_WORKSPACE
+    assert f(vp(A), 1000, 1.0, 1e-4, vp(B + 8), 0, vp(C), need, None) == nb.NBODY_ERR_ALIGNMENT
+    assert f(vp(A), 1000, 1.0, 1e-4, vp(A + 16), 0, vp(C), need, None) == nb.NBODY_ERR_ALIAS
+    assert f(vp(A), 1000, 1.0, 1e-4, vp(B), 0, vp(A + 64), need, None) == nb.NBODY_ERR_ALIAS
+    assert f(vp(A), nb.NBODY_MAX_N, 1.0, 1e-4, vp(B), 0, vp(C), 1 << 62, None) == nb.NBODY_ERR_INVALID_ARG
+
+
 def test_range_validation(lib):
     f = lib.nbody_accel_range
     assert f(vp(A), 100, 0, 0, 1.0, 1e-4, vp(B), -1, None) == nb.NBODY_OK          # empty share

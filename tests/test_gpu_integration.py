@@ -265,3 +265,97 @@ def test_energy_from_potential(name):
     assert abs(e["M"] - direct["M"]) <= 1e-13 * direct["M"]
     for k in ("Px", "Py", "Pz"):
         assert abs(e[k] - direct[k]) <= 1e-13 * mv, k
+
+
+# ---------------------------------------------------------------------------
+# Pair-symmetric pass with the potential in accel.w
+# ---------------------------------------------------------------------------
+
+# the plain pair-symmetric variant with the same (K, KP, waves) panel shape as
+# each potential variant: their xyz arithmetic and order are the same
+SYM_POT_TWIN = {0: 8, 1: 9, 2: 10, 3: 9}
+
+
+def gpu_sym(pm_np, G, eps2, variant, pot):
+    t = to_dev(pm_np)
+    n = pm_np.shape[0]
+    out = torch.full_like(t, float("nan"))
+    if pot:
+        need = nb.nbody_accel_symmetric_potential_workspace_bytes(n, variant)
+    else:
+        need = nb.nbody_accel_symmetric_workspace_bytes(n, variant)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=DEV)
+    if pot:
+        nb.nbody_accel_symmetric_potential(t, G, eps2, out, ws, variant)
+    else:
+        nb.nbody_accel_symmetric(t, G, eps2, out, ws, variant)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def check_potential(a, pm, G, eps2, rows, what):
+    pos, mass = oracle.split_posmass(pm)
+    ref = oracle.potential_rows(pos, mass, float(F32(G)), float(F32(eps2)), rows)
+    got = a[rows, 3].astype(np.float64)
+    l2 = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    worst = np.max(np.abs(got - ref) / np.abs(ref))
+    log(f"  potential {what}: rel L2 {l2:.2e}, worst {worst:.2e}")
+    assert l2 <= 1e-6 and worst <= 1e-5
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 65, 1000, 2048, 2049, 5000])
+def test_symmetric_potential_every_variant(n):
+    """Every potential variant: xyz bitwise equal to the plain pair-symmetric
+    pass of the same panel shape, xyz against the oracle's acceleration and w
+    against the oracle's potential (self term excluded)."""
+    pm, _ = workloads.plummer(n, seed=200 + n) if n > 3 else workloads.uniform_cube(n, seed=n)
+    G, eps2 = 1.25, 1e-4
+    pos, mass = oracle.split_posmass(pm)
+    ref = oracle.accel(pos, mass, float(F32(G)), float(F32(eps2)))
+    for v in range(nb.nbody_accel_symmetric_potential_variant_count()):
+        log(f"n={n} potential variant {v}")
+        assert (nb.nbody_accel_symmetric_potential_panel(v)
+                == nb.nbody_accel_symmetric_panel(SYM_POT_TWIN[v]))
+        a = gpu_sym(pm, G, eps2, v, True)
+        plain = gpu_sym(pm, G, eps2, SYM_POT_TWIN[v], False)
+        assert np.array_equal(a[:, :3], plain[:, :3]), v
+        if n == 1:
+            assert np.array_equal(a, np.zeros((1, 4), F32))
+            continue
+        assert_parity(a, ref, f"symmetric potential n={n} v={v}")
+        check_potential(a, pm, G, eps2, np.arange(n), f"n={n} v={v}")
+
+
+def test_symmetric_potential_energy_plummer16k():
+    """The checkpoint path: pair-symmetric pass with potentials, then the O(N)
+    energy from them, against the oracle's energy."""
+    w = workloads.WORKLOADS["plummer16k"]
+    pm, vel = workloads.make("plummer16k")
+    a = to_dev(gpu_sym(pm, w.G, w.eps2, -1, True))
+    ws = torch.empty(nb.nbody_energy_from_potential_workspace_bytes(w.n), dtype=torch.uint8,
+                     device=DEV)
+    stats = torch.zeros(8, dtype=torch.float64, device=DEV)
+    nb.nbody_energy_from_potential(to_dev(pm), to_dev(vel), a, ws, stats)
+    torch.cuda.synchronize()
+    e = dict(zip(nb.ENERGY_FIELDS, stats.cpu().tolist()))
+    r = ref_energy(pm, vel, w.G, w.eps2)
+    log(f"plummer16k W: symmetric potential {e['W']:.12e}, oracle {r['W']:.12e}")
+    assert abs(e["W"] - r["W"]) <= 2e-6 * abs(r["W"])
+    assert abs(e["E"] - r["E"]) <= 2e-6 * abs(r["E"])
+
+
+def test_symmetric_potential_plummer1m_sampled():
+    """Full size, the variant the library picks for 2^20 bodies: xyz bitwise
+    equal to the plain pass's default, sampled rows of xyz and of the
+    potential against the oracle."""
+    w = workloads.WORKLOADS["plummer1m"]
+    pm, _ = workloads.make("plummer1m")
+    a = gpu_sym(pm, w.G, w.eps2, -1, True)
+    plain = gpu_sym(pm, w.G, w.eps2, -1, False)
+    assert np.array_equal(a[:, :3], plain[:, :3])      # default variants share a panel shape
+    rows = np.unique(np.concatenate([np.arange(64), np.arange(w.n - 64, w.n),
+                                     np.random.default_rng(7).choice(w.n, 192, False)]))
+    pos, mass = oracle.split_posmass(pm)
+    ref = oracle.accel_rows(pos, mass, w.G, float(F32(w.eps2)), rows)
+    assert_parity(a[rows], ref, "symmetric potential plummer1m")
+    check_potential(a, pm, w.G, w.eps2, rows, "plummer1m")
