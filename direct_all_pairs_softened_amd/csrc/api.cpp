@@ -255,7 +255,8 @@ static int sym_pass(const float *posmass, int64_t n, float G, float eps2, float 
   if (v >= nbody::symmetric_variant_count(pot)) return NBODY_ERR_INVALID_ARG;
   if (n == 0) return NBODY_OK;
   const int64_t P = nbody::symmetric_panels(n, v, pot);
-  if (P * (P + 1) / 2 > INT32_MAX) return NBODY_ERR_INVALID_ARG;
+  // one block per panel pair, the grid rounded up to whole XCD stretches
+  if (P * (P + 1) / 2 > INT32_MAX - 8) return NBODY_ERR_INVALID_ARG;
   if (!posmass || !accel_out) return NBODY_ERR_INVALID_ARG;
   if (!aligned(posmass, 16) || !aligned(accel_out, 16)) return NBODY_ERR_ALIGNMENT;
   const size_t need = nbody::symmetric_workspace_bytes(n, v, pot);
@@ -378,7 +379,7 @@ int nbody_energy(const float *posmass, const float *vel, int64_t n, float G, flo
   if (!n_ok(n)) return NBODY_ERR_INVALID_ARG;
   if (int s = check_consts(G, eps2)) return s;
   if (n == 0) return NBODY_OK;  // stats_out is left untouched
-  if (nbody::energy_pair_tasks(n) > INT32_MAX) return NBODY_ERR_INVALID_ARG;
+  if (nbody::energy_pair_tasks(n) > INT32_MAX - 8) return NBODY_ERR_INVALID_ARG;
   if (!posmass || !vel || !stats_out) return NBODY_ERR_INVALID_ARG;
   if (!aligned(stats_out, 8)) return NBODY_ERR_ALIGNMENT;
   if (!aligned(posmass, 16) || !aligned(vel, 16)) return NBODY_ERR_ALIGNMENT;

@@ -110,13 +110,16 @@ __device__ __forceinline__ double pair_potential_task(const float4 *__restrict__
   return acc;
 }
 
-// One block per panel pair (I, J), I <= J: task_out[t] = sum over the pairs
-// of m_i m_j / sqrt(r^2 + eps^2), each unordered pair once.
+// One block per panel pair (I, J), I <= J, in the XCD-aware order of
+// PanelOrder: task_out[t] = sum over the pairs of m_i m_j / sqrt(r^2 + eps^2),
+// each unordered pair once, t the pair's number in that order.
 __global__ __launch_bounds__(kPairW *kWave) void energy_pairs_kernel(
-    const float4 *__restrict__ pm, int n, float eps2, double *__restrict__ task_out) {
+    const float4 *__restrict__ pm, int n, PanelOrder order, float eps2,
+    double *__restrict__ task_out) {
   __shared__ double red[kPairW * kWave];
   int I, J;
-  decode_panel_pair(blockIdx.x, I, J);
+  long long t;
+  if (!panel_pair_of_block(order, blockIdx.x, I, J, t)) return;  // whole block: no barrier skipped
   double acc = I == J ? pair_potential_task<true>(pm, n, I, J, eps2)
                       : pair_potential_task<false>(pm, n, I, J, eps2);
   const int tid = threadIdx.x;
@@ -127,7 +130,7 @@ __global__ __launch_bounds__(kPairW *kWave) void energy_pairs_kernel(
     __syncthreads();
   }
   // a diagonal task met every pair twice; halving is exact
-  if (tid == 0) task_out[blockIdx.x] = I == J ? 0.5 * red[0] : red[0];
+  if (tid == 0) task_out[t] = I == J ? 0.5 * red[0] : red[0];
 }
 
 __global__ __launch_bounds__(kFinalThreads) void energy_final_kernel(
@@ -215,8 +218,9 @@ hipError_t launch_energy(const float *posmass, const float *vel, int n, float G,
                      block_out);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(energy_pairs_kernel, dim3((unsigned)tasks), dim3(kPairW * kWave), 0, stream,
-                     pm, n, eps2, task_out);
+  const PanelOrder order = panel_order((n + kPairPanel - 1) / kPairPanel);
+  hipLaunchKernelGGL(energy_pairs_kernel, dim3((unsigned)(kXcds * order.per_xcd)),
+                     dim3(kPairW * kWave), 0, stream, pm, n, order, eps2, task_out);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(energy_final_kernel, dim3(1), dim3(kFinalThreads), 0, stream, block_out,

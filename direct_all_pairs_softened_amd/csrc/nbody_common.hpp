@@ -81,13 +81,75 @@ __device__ __forceinline__ float rotate_lanes(float v) {
       __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x13C, 0xf, 0xf, false));
 }
 
-// Panel pair (I, J), I <= J, enumerated as t = J (J + 1) / 2 + I.
-__device__ __forceinline__ void decode_panel_pair(long long t, int &I, int &J) {
+// Largest j with j (j + 1) / 2 <= t.
+__host__ __device__ inline long long tri_root(long long t) {
   long long j = (long long)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
-  while (j * (j + 1) / 2 > t) --j;
+  while (j > 0 && j * (j + 1) / 2 > t) --j;
   while ((j + 1) * (j + 2) / 2 <= t) ++j;
-  J = (int)j;
-  I = (int)(t - j * (j + 1) / 2);
+  return j;
+}
+
+// Order of the P (P + 1) / 2 panel pairs (I, J), I <= J < P, of the
+// pair-symmetric passes, and which blocks take them.
+//
+// Pairs are numbered in tile-column order: the panels are grouped in tiles
+// of S x S panel pairs; tile column c holds the pairs with
+// J in [cS, cS + cols), cols = min(S, P - cS), which are the pairs numbered
+// from Sc (Sc + 1) / 2 on (exactly as in the plain J-major triangle).  Inside
+// a tile column come the full tiles of rows a = 0 .. c - 1 (S x cols pairs
+// each, J-major), then the triangle of the diagonal tile.  A stretch of
+// consecutive numbers therefore touches about S + stretch / S panels.
+//
+// Blocks go to the 8 XCDs of the chip round robin (block b to XCD b % 8), so
+// block b takes pair number (b % 8) * per_xcd + b / 8: each XCD walks its
+// own contiguous stretch of the order, and the panels its concurrent blocks
+// read stay in that XCD's L2.  Which block computes a pair does not change
+// any sum: every pair writes its own workspace slot.
+struct PanelOrder {
+  int P;               // panels
+  int S;               // tile side in panels
+  long long pairs;     // P (P + 1) / 2
+  long long per_xcd;   // ceil(pairs / 8): grid = 8 * per_xcd blocks
+};
+
+constexpr int kXcds = 8;
+constexpr int kPanelTile = 32;
+
+inline PanelOrder panel_order(long long P) {
+  PanelOrder o;
+  o.P = (int)P;
+  o.S = kPanelTile;
+  o.pairs = P * (P + 1) / 2;
+  o.per_xcd = (o.pairs + kXcds - 1) / kXcds;
+  return o;
+}
+
+// Pair number t (0 <= t < pairs) of the order above.
+__host__ __device__ inline void panel_pair_of(const PanelOrder &o, long long t, int &I, int &J) {
+  const long long S = o.S;
+  const long long c = tri_root(t) / S;             // tile column of t
+  const long long u = t - (S * c) * (S * c + 1) / 2;  // offset inside the tile column
+  const long long cols = (o.P - S * c) < S ? (o.P - S * c) : S;
+  if (u < c * S * cols) {                          // full tile of row a, J-major
+    const long long a = u / (S * cols), v = u % (S * cols);
+    J = (int)(S * c + v / S);
+    I = (int)(S * a + v % S);
+  } else {                                         // diagonal tile, I <= J
+    const long long v = u - c * S * cols;
+    const long long j = tri_root(v);
+    J = (int)(S * c + j);
+    I = (int)(S * c + v - j * (j + 1) / 2);
+  }
+}
+
+// The pair block b takes; false for the few blocks past the last pair.
+__host__ __device__ inline bool panel_pair_of_block(const PanelOrder &o, long long b, int &I,
+                                                    int &J, long long &t) {
+  const long long k = b / kXcds;
+  t = (b % kXcds) * o.per_xcd + k;
+  if (k >= o.per_xcd || t >= o.pairs) return false;
+  panel_pair_of(o, t, I, J);
+  return true;
 }
 
 // ---------------------------------------------------------------------------

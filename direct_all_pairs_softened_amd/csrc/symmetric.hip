@@ -8,7 +8,8 @@
 //
 // Decomposition.  Bodies are cut into P panels of B = 64 * W * K bodies (the
 // tail padded with zero-mass copies of the last body).  A block takes one
-// task (I, J), I <= J, of the P(P+1)/2 panel pairs:
+// task (I, J), I <= J, of the P(P+1)/2 panel pairs (in the XCD-aware tile
+// order of PanelOrder, which keeps each XCD's panels in its own L2):
 //  - wave w holds K bodies of panel I per lane in registers (its i-group);
 //  - panel J is walked in sweeps of 64 * KP bodies.  For a sweep each lane
 //    loads KP j-bodies, then 64 steps each evaluate the lane's K x KP pairs
@@ -210,14 +211,17 @@ __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, i
   }
 }
 
-// One block per task; blockIdx.x = J (J + 1) / 2 + I enumerates I <= J.
+// One block per task (panel pair); PanelOrder gives the pair of each block
+// (every XCD walks a contiguous stretch of tile-ordered pairs).
 template <int K, int KP, int W, int OCC, int IL, bool POT>
 __global__ __launch_bounds__(W *kWave) __attribute__((amdgpu_waves_per_eu(OCC))) void
-symmetric_task_kernel(const float4 *__restrict__ pm, int n, int P, float eps2,
+symmetric_task_kernel(const float4 *__restrict__ pm, int n, PanelOrder order, float eps2,
                       float *__restrict__ part) {
   __shared__ float csum[W][KP][sym_sums<POT>()][kWave];
   int Ic, Jc;
-  decode_panel_pair(blockIdx.x, Ic, Jc);
+  long long t;
+  if (!panel_pair_of_block(order, blockIdx.x, Ic, Jc, t)) return;  // whole block: no barrier skipped
+  const int P = order.P;
   if (Ic == Jc)
     sym_task<K, KP, W, IL, POT, true>(pm, n, Ic, Jc, P, eps2, part, csum);
   else
@@ -328,7 +332,8 @@ hipError_t launch_symmetric(const float *posmass, int n, float G, float eps2, fl
                             int v, bool pot, void *workspace, hipStream_t stream) {
   const int B = symmetric_panel(v, pot);
   const int P = (int)symmetric_panels(n, v, pot);
-  const long long tasks = (long long)P * (P + 1) / 2;
+  const PanelOrder order = panel_order(P);
+  const long long blocks = kXcds * order.per_xcd;
   float *part = reinterpret_cast<float *>(workspace);
   const float4 *pm = reinterpret_cast<const float4 *>(posmass);
   if (!pot) {
@@ -336,7 +341,7 @@ hipError_t launch_symmetric(const float *posmass, int n, float G, float eps2, fl
 #define X(id, K, KP, W, OCC, IL)                                                       \
   case id:                                                                             \
     hipLaunchKernelGGL((symmetric_task_kernel<K, KP, W, OCC, IL, false>),              \
-                       dim3((unsigned)tasks), dim3(W * kWave), 0, stream, pm, n, P, eps2, \
+                       dim3((unsigned)blocks), dim3(W * kWave), 0, stream, pm, n, order, eps2, \
                        part);                                                          \
     break;
       NBODY_SYM_VARIANTS(X)
@@ -349,7 +354,7 @@ hipError_t launch_symmetric(const float *posmass, int n, float G, float eps2, fl
 #define X(id, K, KP, W, OCC)                                                           \
   case id:                                                                             \
     hipLaunchKernelGGL((symmetric_task_kernel<K, KP, W, OCC, 1, true>),                \
-                       dim3((unsigned)tasks), dim3(W * kWave), 0, stream, pm, n, P, eps2, \
+                       dim3((unsigned)blocks), dim3(W * kWave), 0, stream, pm, n, order, eps2, \
                        part);                                                          \
     break;
       NBODY_SYM_POT_VARIANTS(X)
