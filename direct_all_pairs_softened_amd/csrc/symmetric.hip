@@ -25,7 +25,8 @@
 // Output of a task: part[I][J] = panel I's sums from panel J and, for I < J,
 // part[J][I] = panel J's sums from panel I.  A second kernel forms
 // a_i = G * sum_{J = 0 .. P-1} part[I(i)][J][i], ascending J.
-// Workspace: part float[P][P][3][B], i.e. 12 N^2 / B bytes.
+// Workspace: part float[P][P][NC][B], NC = 3 sums per body (4 with the
+// potential), i.e. 12 N^2 / B bytes (16 N^2 / B).
 //
 // Per pair (two interactions) a lane issues 16 FP32 VALU ops and one
 // v_rsq_f32, plus 7 / K DPP moves; the one-sided kernel issues 12 ops and one
