@@ -23,6 +23,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 from collections import defaultdict
 
@@ -39,11 +40,21 @@ KERNEL_SOURCES = {
              "direct_all_pairs_softened_amd/csrc/nbody_common.hpp"),
 }
 COPY_KERNEL_HINTS = ("copyBuffer", "copy", "Copy")
+
+
+def _code_only(text: str) -> str:
+    """C++ source without comments, whitespace runs collapsed: edits to
+    comments or layout do not count as a change of the kernel."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash(path: str) -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[path]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
