@@ -126,6 +126,25 @@ def test_decimal_brute_force_small():
         assert _rel(a[i], ref) <= 1e-14
 
 
+def test_summation_rounding_is_small():
+    """The oracle's running double sums against an exactly rounded sum
+    (math.fsum) of double-precision terms, over all 16384 bodies of the
+    Plummer workload for 48 sampled rows: a sum that lost digits (float
+    accumulation, a term dropped or doubled) would show far above 1e-12."""
+    pm, _ = workloads.make("plummer16k")
+    pos, mass = oracle.split_posmass(pm)
+    eps2 = float(np.float32(1e-4))
+    rows = np.random.default_rng(11).choice(pos.shape[0], 48, replace=False)
+    a = oracle.accel_rows(pos, mass, 1.0, eps2, rows.astype(np.int64))
+    for r, i in enumerate(rows):
+        d = pos - pos[i]
+        d2 = (d * d).sum(axis=1) + eps2
+        w = mass / (d2 * np.sqrt(d2))
+        w[i] = 0.0
+        exact = [math.fsum(w * d[:, k]) for k in range(3)]
+        assert _rel(a[r], exact) <= 1e-12, i
+
+
 # --------------------------------------------------------------------------
 # Invariants on the project's workloads
 # --------------------------------------------------------------------------
