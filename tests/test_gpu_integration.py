@@ -359,3 +359,33 @@ def test_symmetric_potential_plummer1m_sampled():
     ref = oracle.accel_rows(pos, mass, w.G, float(F32(w.eps2)), rows)
     assert_parity(a[rows], ref, "symmetric potential plummer1m")
     check_potential(a, pm, w.G, w.eps2, rows, "plummer1m")
+
+
+def test_circular_binary_one_orbit():
+    """Equal-mass circular binary (d = 1, eps^2 = 1e-4, omega^2 = G (m1 + m2) /
+    (d^2 + eps^2)^{3/2}) for one period at dt = T/1000 with the GPU's KDK
+    step: the separation stays within (omega dt)^2 plus float32 rounding of d,
+    and the bodies come back near their start (phase error O((omega dt)^2))."""
+    eps2 = 1e-4
+    m = 0.5
+    omega = math.sqrt(2 * m / (1.0 + eps2) ** 1.5)
+    period = 2 * math.pi / omega
+    steps = 1000
+    dt = float(F32(period / steps))
+    pm0 = np.array([[-0.5, 0, 0, m], [0.5, 0, 0, m]], F32)
+    v0 = np.array([[0, -omega * 0.5, 0, 0], [0, omega * 0.5, 0, 0]], F32)
+    pm, vel = to_dev(pm0), to_dev(v0)
+    acc = torch.empty_like(pm)
+    nb.nbody_accel(pm, 1.0, eps2, acc)
+    worst = 0.0
+    for k in range(steps):
+        nb.kdk_step(pm, vel, acc, 1.0, eps2, dt)
+        if (k + 1) % 50 == 0:
+            x = pm.cpu().numpy()[:, :3].astype(np.float64)
+            worst = max(worst, abs(np.linalg.norm(x[1] - x[0]) - 1.0))
+    torch.cuda.synchronize()
+    x = pm.cpu().numpy()[:, :3].astype(np.float64)
+    log(f"circular binary: max |d - 1| {worst:.2e} (bound {(omega * dt) ** 2:.2e}), "
+        f"return error {np.abs(x - pm0[:, :3]).max():.2e}")
+    assert worst <= (omega * dt) ** 2 + 1e-5
+    assert np.abs(x - pm0[:, :3]).max() <= 2e-3

@@ -86,6 +86,19 @@ def test_uniform1k_workload():
     assert net / (m * np.linalg.norm(ag, axis=1)).sum() <= 1e-6
 
 
+def test_translated_inputs_stay_within_parity():
+    """Translation invariance: the pass on positions shifted by
+    c = (0.25, -0.5, 0.125) (the shift rounded to float32 per coordinate)
+    against the oracle on the unshifted inputs, with the parity bar."""
+    w = workloads.WORKLOADS["uniform1k"]
+    pm, _ = workloads.make("uniform1k")
+    shifted = pm.copy()
+    shifted[:, :3] = (pm[:, :3].astype(np.float64) + np.array([0.25, -0.5, 0.125])).astype(F32)
+    ref = ref_accel(pm, w.G, w.eps2)
+    assert_parity(gpu_accel(shifted, w.G, w.eps2), ref, "uniform1k shifted, one-sided")
+    assert_parity(sym_accel(shifted, w.G, w.eps2), ref, "uniform1k shifted, pair-symmetric")
+
+
 def test_plummer16k_full_parity():
     w = workloads.WORKLOADS["plummer16k"]
     pm, _ = workloads.make("plummer16k")
