@@ -45,9 +45,10 @@ namespace {
 // arithmetic of each pair, and its order of accumulation, do not depend on IL.
 // POT adds the potential sums: i gains m_j inv, j gains m_i inv (two more
 // multiply-adds per pair; the force arithmetic is unchanged).
-template <int K, int IL, bool POT>
+template <int K, int IL, bool POT, int ML>
 __device__ __forceinline__ void sym_step(const float (&xi)[K], const float (&yi)[K],
-                                         const float (&zi)[K], const float (&mi)[K], float xj,
+                                         const float (&zi)[K], const float (&mi)[K],
+                                         const float *mil, float xj,
                                          float yj, float zj, float mj, float eps2, float (&ax)[K],
                                          float (&ay)[K], float (&az)[K], float (&ap)[K],
                                          float &cx, float &cy, float &cz, float &cp) {
@@ -81,11 +82,12 @@ __device__ __forceinline__ void sym_step(const float (&xi)[K], const float (&yi)
     }
 #pragma unroll
     for (int q = 0; q < IL; ++q) {
-      const float si = mi[h + q] * w[q];
+      const float m = (h + q >= K - ML) ? mil[(h + q - (K - ML)) * kWave] : mi[h + q];
+      const float si = m * w[q];
       cx = __builtin_fmaf(si, dx[q], cx);
       cy = __builtin_fmaf(si, dy[q], cy);
       cz = __builtin_fmaf(si, dz[q], cz);
-      if constexpr (POT) cp = __builtin_fmaf(mi[h + q], inv[q], cp);
+      if constexpr (POT) cp = __builtin_fmaf(m, inv[q], cp);
     }
   }
 }
@@ -97,10 +99,10 @@ constexpr int sym_sums() {
   return POT ? 4 : 3;
 }
 
-template <int K, int KP, int W, int IL, bool POT, bool DIAG>
+template <int K, int KP, int W, int IL, bool POT, int ML, bool DIAG>
 __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, int I, int J,
                                          int P, float eps2, float *__restrict__ part,
-                                         float (*csum)[KP][sym_sums<POT>()][kWave]) {
+                                         float (*csum)[KP][sym_sums<POT>()][kWave], float *mis) {
   constexpr int B = W * kWave * K;
   constexpr int JG = kWave * KP;
   constexpr int NG = B / JG;
@@ -118,6 +120,9 @@ __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, i
     yi[q] = b.y;
     zi[q] = b.z;
     mi[q] = i < n ? b.w : 0.0f;
+    if constexpr (ML > 0) {
+      if (q >= K - ML) mis[(wave * ML + q - (K - ML)) * kWave + lane] = mi[q];
+    }
     ax[q] = 0.0f;
     ay[q] = 0.0f;
     az[q] = 0.0f;
@@ -143,8 +148,13 @@ __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, i
 #pragma unroll
       for (int p = 0; p < KP; ++p) {
         if constexpr (!DIAG) {
-          sym_step<K, IL, POT>(xi, yi, zi, mi, xj[p], yj[p], zj[p], mj[p], eps2, ax, ay, az, ap,
-                               cx[p], cy[p], cz[p], cp[p]);
+          // masses kept in LDS are read inside the step: the empty asm that
+          // claims to change the index stops the compiler from hoisting the
+          // reads out of the loop into registers
+          int mio = wave * ML * kWave + lane;
+          if constexpr (ML > 0) asm volatile("" : "+v"(mio));
+          sym_step<K, IL, POT, ML>(xi, yi, zi, mi, mis + mio, xj[p], yj[p], zj[p], mj[p], eps2,
+                                   ax, ay, az, ap, cx[p], cy[p], cz[p], cp[p]);
         } else {
 #pragma unroll
         for (int q = 0; q < K; ++q) {
@@ -214,19 +224,20 @@ __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, i
 
 // One block per task (panel pair); PanelOrder gives the pair of each block
 // (every XCD walks a contiguous stretch of tile-ordered pairs).
-template <int K, int KP, int W, int OCC, int IL, bool POT>
+template <int K, int KP, int W, int OCC, int IL, bool POT, int ML>
 __global__ __launch_bounds__(W *kWave) __attribute__((amdgpu_waves_per_eu(OCC))) void
 symmetric_task_kernel(const float4 *__restrict__ pm, int n, PanelOrder order, float eps2,
                       float *__restrict__ part) {
   __shared__ float csum[W][KP][sym_sums<POT>()][kWave];
+  __shared__ float mis[ML > 0 ? W * ML * kWave : 1];
   int Ic, Jc;
   long long t;
   if (!panel_pair_of_block(order, blockIdx.x, Ic, Jc, t)) return;  // whole block: no barrier skipped
   const int P = order.P;
   if (Ic == Jc)
-    sym_task<K, KP, W, IL, POT, true>(pm, n, Ic, Jc, P, eps2, part, csum);
+    sym_task<K, KP, W, IL, POT, ML, true>(pm, n, Ic, Jc, P, eps2, part, csum, mis);
   else
-    sym_task<K, KP, W, IL, POT, false>(pm, n, Ic, Jc, P, eps2, part, csum);
+    sym_task<K, KP, W, IL, POT, ML, false>(pm, n, Ic, Jc, P, eps2, part, csum, mis);
 }
 
 // a_i = G sum_J part[I][J][c][b] over J ascending; with POT the fourth sum is
@@ -250,49 +261,56 @@ __global__ __launch_bounds__(256) void symmetric_reduce_kernel(const float *__re
   out[i] = make_float4(G * sx, G * sy, G * sz, POT ? -G * sp : 0.0f);
 }
 
-// (id, K, KP, waves, occupancy target, interleave width); panel B =
-// 64 * waves * K.  Interleave widths 2 and 4 (variants 12, 13) measured the
-// same as 1 on MI355X: under the 6-waves-per-SIMD register budget the
-// compiler schedules the pairs one after the other either way.
+// (id, K, KP, waves, occupancy target, interleave width, i-masses in LDS);
+// panel B = 64 * waves * K.  Interleave widths 2 and 4 (variants 12, 13)
+// measured the same as 1 on MI355X: under the 6-waves-per-SIMD register
+// budget the compiler schedules the pairs one after the other either way.
+// Variant 14 keeps 5 of its 8 i-masses in LDS (read once per pair inside the
+// step), which lets K = 8 fit 72 VGPRs without spilling: 7 waves per SIMD
+// instead of 6, and 193 against 206 ms at 2^20 bodies.  Asking for 8 waves
+// instead (64 VGPRs) makes the compiler spill to scratch inside the step
+// loop: 197 ms, and ~9 GB more memory traffic per pass.
 #define NBODY_SYM_VARIANTS(X) \
-  X(0, 8, 2, 4, 4, 1)         \
-  X(1, 8, 1, 4, 4, 1)         \
-  X(2, 4, 2, 4, 6, 1)         \
-  X(3, 8, 2, 8, 4, 1)         \
-  X(4, 4, 4, 4, 4, 1)         \
-  X(5, 8, 1, 8, 4, 1)         \
-  X(6, 16, 1, 4, 2, 1)        \
-  X(7, 12, 1, 4, 3, 1)        \
-  X(8, 8, 1, 2, 4, 1)         \
-  X(9, 8, 1, 4, 6, 1)         \
-  X(10, 6, 1, 4, 5, 1)        \
-  X(11, 16, 1, 2, 2, 1)       \
-  X(12, 8, 1, 4, 6, 4)        \
-  X(13, 8, 1, 4, 6, 2)
+  X(0, 8, 2, 4, 4, 1, 0)        \
+  X(1, 8, 1, 4, 4, 1, 0)        \
+  X(2, 4, 2, 4, 6, 1, 0)        \
+  X(3, 8, 2, 8, 4, 1, 0)        \
+  X(4, 4, 4, 4, 4, 1, 0)        \
+  X(5, 8, 1, 8, 4, 1, 0)        \
+  X(6, 16, 1, 4, 2, 1, 0)       \
+  X(7, 12, 1, 4, 3, 1, 0)       \
+  X(8, 8, 1, 2, 4, 1, 0)        \
+  X(9, 8, 1, 4, 6, 1, 0)        \
+  X(10, 6, 1, 4, 5, 1, 0)       \
+  X(11, 16, 1, 2, 2, 1, 0)      \
+  X(12, 8, 1, 4, 6, 4, 0)       \
+  X(13, 8, 1, 4, 6, 2, 0)       \
+  X(14, 8, 1, 4, 7, 1, 5)
 
 // Variants of the pass that also sums the potential (id, K, KP, waves,
-// occupancy target); the ids are their own (nbody_accel_symmetric_potential).
-// The potential sums take K = 8 to ~96 VGPRs (5 waves per SIMD); asking for
-// 6 waves caps it at 80 VGPRs, with a few spills outside the off-diagonal
-// step loop, and is 14 % faster at 2^20 bodies (229 against 267 ms).
+// occupancy target, i-masses in LDS); the ids are their own
+// (nbody_accel_symmetric_potential).  The potential sums take K = 8 to ~96
+// VGPRs (5 waves per SIMD, variant 3: 266 ms at 2^20 bodies); capping it at
+// 80 (6 waves) leaves a few spills outside the step loop and, with 2 of the
+// i-masses in LDS, takes 216 ms (variant 1).
 #define NBODY_SYM_POT_VARIANTS(X) \
-  X(0, 8, 1, 2, 6)                \
-  X(1, 8, 1, 4, 6)                \
-  X(2, 6, 1, 4, 6)                \
-  X(3, 8, 1, 4, 5)
+  X(0, 8, 1, 2, 6, 0)             \
+  X(1, 8, 1, 4, 6, 2)             \
+  X(2, 6, 1, 4, 6, 0)             \
+  X(3, 8, 1, 4, 5, 0)
 
 struct SymVariant {
   int K, KP, W;
 };
 
 const SymVariant kSym[] = {
-#define X(id, K, KP, W, OCC, IL) {K, KP, W},
+#define X(id, K, KP, W, OCC, IL, ML) {K, KP, W},
     NBODY_SYM_VARIANTS(X)
 #undef X
 };
 
 const SymVariant kSymPot[] = {
-#define X(id, K, KP, W, OCC) {K, KP, W},
+#define X(id, K, KP, W, OCC, ML) {K, KP, W},
     NBODY_SYM_POT_VARIANTS(X)
 #undef X
 };
@@ -306,14 +324,14 @@ int symmetric_variant_count(bool pot) {
 }
 
 // Measured on MI355X (force-pass sweeps): 8 i-bodies and 1 j-body per lane
-// in 4-wave blocks is fastest at 1e5-1e6 bodies; 1024-body panels (2-wave
-// blocks) give more panel pairs at the low end, 2048-body panels halve the
-// workspace at the high end.  Below ~5e4 bodies there are too few panel pairs
+// is fastest from 1e5 bodies on; 1024-body panels (2-wave blocks) give more
+// panel pairs at the low end, 2048-body panels at 7 waves per SIMD are
+// fastest from ~2e5 bodies and halve the workspace.  Below ~5e4 bodies there are too few panel pairs
 // to fill the chip and the one-sided nbody_accel is faster.  The potential
 // variants follow the same split by n.
 int symmetric_variant_for_n(int64_t n, bool pot) {
-  if (pot) return n <= 300000 ? 0 : 1;
-  return n <= 300000 ? 8 : 9;
+  if (pot) return n <= 200000 ? 0 : 1;
+  return n <= 200000 ? 8 : 14;
 }
 
 int symmetric_panel(int v, bool pot) {
@@ -342,9 +360,9 @@ hipError_t launch_symmetric(const float *posmass, int n, float G, float eps2, fl
   const float4 *pm = reinterpret_cast<const float4 *>(posmass);
   if (!pot) {
     switch (v) {
-#define X(id, K, KP, W, OCC, IL)                                                       \
+#define X(id, K, KP, W, OCC, IL, ML)                                                   \
   case id:                                                                             \
-    hipLaunchKernelGGL((symmetric_task_kernel<K, KP, W, OCC, IL, false>),              \
+    hipLaunchKernelGGL((symmetric_task_kernel<K, KP, W, OCC, IL, false, ML>),          \
                        dim3((unsigned)blocks), dim3(W * kWave), 0, stream, pm, n, order, eps2, \
                        part);                                                          \
     break;
@@ -355,9 +373,9 @@ hipError_t launch_symmetric(const float *posmass, int n, float G, float eps2, fl
     }
   } else {
     switch (v) {
-#define X(id, K, KP, W, OCC)                                                           \
+#define X(id, K, KP, W, OCC, ML)                                                       \
   case id:                                                                             \
-    hipLaunchKernelGGL((symmetric_task_kernel<K, KP, W, OCC, 1, true>),                \
+    hipLaunchKernelGGL((symmetric_task_kernel<K, KP, W, OCC, 1, true, ML>),            \
                        dim3((unsigned)blocks), dim3(W * kWave), 0, stream, pm, n, order, eps2, \
                        part);                                                          \
     break;

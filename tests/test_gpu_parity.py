@@ -411,10 +411,11 @@ def test_lds_free_variants_bitwise_equal_lds(stream_v, lds_v):
 
 def test_symmetric_interleave_variants_bitwise_equal():
     """Variants that differ only in the issue order of independent pairs
-    (interleave width) compute the same sums."""
+    (interleave width) or in where the i-masses live (14: five of them in
+    LDS, 7 waves per SIMD) compute the same sums."""
     pm, _ = workloads.uniform_cube(6000, seed=55, masses="lognormal")
     base = sym_accel(pm, eps2=1e-5, variant=9)
-    for v in (12, 13):
+    for v in (12, 13, 14):
         assert nb.nbody_accel_symmetric_panel(v) == nb.nbody_accel_symmetric_panel(9)
         assert np.array_equal(sym_accel(pm, eps2=1e-5, variant=v), base), v
 
