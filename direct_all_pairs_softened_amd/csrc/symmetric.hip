@@ -3,22 +3,28 @@
 // from i is the term on i from j times -m_i/m_j).  The atomics tutorial (CUDA
 // programming part 9, its neighbour-list example) runs the same symmetric
 // half loop but has to add the second body's share with atomicAdd.  Here the
-// share is carried in registers and added in a fixed order, so the result is
-// bitwise reproducible and there are no atomics.
+// share is carried by the j-body's own state and added in a fixed order, so
+// the result is bitwise reproducible and there are no atomics.
 //
 // Decomposition.  Bodies are cut into P panels of B = 64 * W * K bodies (the
 // tail padded with zero-mass copies of the last body).  A block takes one
 // task (I, J), I <= J, of the P(P+1)/2 panel pairs (in the XCD-aware tile
 // order of PanelOrder, which keeps each XCD's panels in its own L2):
 //  - wave w holds K bodies of panel I per lane in registers (its i-group);
-//  - panel J is walked in sweeps of 64 * KP bodies.  For a sweep each lane
-//    loads KP j-bodies, then 64 steps each evaluate the lane's K x KP pairs
-//    and rotate the j-state (x, y, z, m and the j-side sums) one lane along
-//    the wave with a DPP wave_ror:1 move.  After 64 steps every j-body has
-//    met every i-body of the wave and its state is back in its home lane;
+//  - panel J is walked in sweeps of 64 * KP bodies.  Over the 64 steps of a
+//    sweep every lane meets every j-body of the sweep once, evaluating its
+//    K x KP pairs per step;
 //  - pair term: r = x_j - x_i, inv = rsq(|r|^2 + eps^2), w = inv^3;
-//    i gains m_j w r (register sum), j gains -m_i w r (rotating sum);
+//    i gains m_j w r (register sum), j gains -m_i w r (the j-side sum);
 //  - the W waves' j-side sums are added in ascending wave order through LDS.
+// The j-state (x, y, z, m and the j-side sums) travels in one of two ways:
+//  - rotated (JL = 0): each lane loads KP j-bodies and after each step moves
+//    the j-state one lane along the wave with a DPP wave_ror:1 move (7 / K
+//    moves per pair, VALU instructions that cannot dual-issue);
+//  - LDS-carried (JL > 0, KP = 1): the j-bodies and their sums sit in the
+//    wave's LDS; each step a lane reads the body it meets, sums its K pairs'
+//    j-side terms in registers, then adds them to the body's slot (a read, 3
+//    adds and a write: the adds dual-issue, and no DPP moves are left).
 // Diagonal tasks (I = J) use the one-sided sum (j over the whole panel,
 // self term exactly 0) and no j-side sums.
 //
@@ -29,8 +35,8 @@
 // potential), i.e. 12 N^2 / B bytes (16 N^2 / B).
 //
 // Per pair (two interactions) a lane issues 16 FP32 VALU ops and one
-// v_rsq_f32, plus 7 / K DPP moves; the one-sided kernel issues 12 ops and one
-// v_rsq_f32 per interaction.
+// v_rsq_f32, plus 7 / K DPP moves (rotated) or 3 / K adds (LDS-carried); the
+// one-sided kernel issues 12 ops and one v_rsq_f32 per interaction.
 #include "nbody_common.hpp"
 #include "nbody_internal.hpp"
 
@@ -45,7 +51,7 @@ namespace {
 // arithmetic of each pair, and its order of accumulation, do not depend on IL.
 // POT adds the potential sums: i gains m_j inv, j gains m_i inv (two more
 // multiply-adds per pair; the force arithmetic is unchanged).
-template <int K, int IL, bool POT, int ML>
+template <int K, int IL, bool POT, int ML, bool FRESH = false>
 __device__ __forceinline__ void sym_step(const float (&xi)[K], const float (&yi)[K],
                                          const float (&zi)[K], const float (&mi)[K],
                                          const float *mil, float xj,
@@ -84,10 +90,17 @@ __device__ __forceinline__ void sym_step(const float (&xi)[K], const float (&yi)
     for (int q = 0; q < IL; ++q) {
       const float m = (h + q >= K - ML) ? mil[(h + q - (K - ML)) * kWave] : mi[h + q];
       const float si = m * w[q];
-      cx = __builtin_fmaf(si, dx[q], cx);
-      cy = __builtin_fmaf(si, dy[q], cy);
-      cz = __builtin_fmaf(si, dz[q], cz);
-      if constexpr (POT) cp = __builtin_fmaf(m, inv[q], cp);
+      if (FRESH && h + q == 0) {  // the j-side sums start at this step
+        cx = si * dx[q];
+        cy = si * dy[q];
+        cz = si * dz[q];
+        if constexpr (POT) cp = m * inv[q];
+      } else {
+        cx = __builtin_fmaf(si, dx[q], cx);
+        cy = __builtin_fmaf(si, dy[q], cy);
+        cz = __builtin_fmaf(si, dz[q], cz);
+        if constexpr (POT) cp = __builtin_fmaf(m, inv[q], cp);
+      }
     }
   }
 }
@@ -99,10 +112,11 @@ constexpr int sym_sums() {
   return POT ? 4 : 3;
 }
 
-template <int K, int KP, int W, int IL, bool POT, int ML, bool DIAG>
+template <int K, int KP, int W, int IL, bool POT, int ML, int JL, bool DIAG>
 __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, int I, int J,
                                          int P, float eps2, float *__restrict__ part,
-                                         float (*csum)[KP][sym_sums<POT>()][kWave], float *mis) {
+                                         float (*csum)[KP][sym_sums<POT>()][kWave], float *mis,
+                                         float4 *jtile, float4 *jsum) {
   constexpr int B = W * kWave * K;
   constexpr int JG = kWave * KP;
   constexpr int NG = B / JG;
@@ -129,6 +143,79 @@ __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, i
     ap[q] = 0.0f;
   }
 
+  if constexpr (JL > 0 && !DIAG) {
+    // The j-state lives in the wave's LDS instead of travelling along the
+    // lanes.  The sweep's 64 j-bodies sit twice in a row in the tile jt, and
+    // step s pairs lane l with entry k = l + s, i.e. body (l + s) mod 64.  The
+    // j-side sums sit in slots js[k] beside them: the lane reads slot k, adds
+    // its K pairs' terms in registers and writes the slot back.  The next
+    // access to slot k is lane l - 1's at step s + 1, an instruction the LDS
+    // executes after this write (one wave's LDS instructions run in issue
+    // order).  Body j's sum of the sweep is js[j] + js[j + 64].
+    static_assert(KP == 1, "LDS j-tiles hold one j-body per lane");
+    constexpr int U = JL;  // steps per unrolled block: LDS offsets are immediates
+    static_assert(kWave % U == 0, "unroll must divide the sweep");
+    float4 *jt = jtile + wave * 2 * kWave;
+    float4 *js = jsum + wave * 2 * kWave;
+    // byte offset of the lane's first LDS mass; the empty asm that claims to
+    // change it every step keeps the mass reads inside the step (it is the
+    // same register in and out, so it costs no instruction)
+    int mio = (wave * ML * kWave + lane) * (int)sizeof(float);
+    for (int g = 0; g < NG; ++g) {
+      const int j = J * B + g * kWave + lane;
+      const float4 b = pm[j < n ? j : n - 1];
+      const float4 jb = make_float4(b.x, b.y, b.z, j < n ? b.w : 0.0f);
+      jt[lane] = jb;
+      jt[lane + kWave] = jb;
+      // a zero made here, so that the compiler has no zero vector to keep
+      // (or spill) across the sweep
+      float z;
+      asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+      js[lane] = make_float4(z, z, z, z);
+      js[lane + kWave] = make_float4(z, z, z, z);
+      // Other lanes read what this lane wrote: no LDS access may be moved
+      // across these points (the empty asm with a memory clobber).
+      asm volatile("" ::: "memory");
+      float4 y = jt[lane];
+      for (int s0 = 0; s0 < kWave; s0 += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int k = lane + s0 + u;
+          const float4 yn = jt[k + 1];  // the next step's j-body (k + 1 <= 127)
+          if constexpr (ML > 0) asm volatile("" : "+v"(mio));
+          const float *mil =
+              reinterpret_cast<const float *>(reinterpret_cast<const char *>(mis) + mio);
+          float tx, ty, tz, tp;
+          sym_step<K, IL, POT, ML, true>(xi, yi, zi, mi, mil, y.x, y.y, y.z, y.w, eps2, ax, ay,
+                                         az, ap, tx, ty, tz, tp);
+          // the slot is read after the step's pairs: its last writer is the
+          // neighbour lane's previous step, already behind this point
+          float4 c = js[k];
+          c.x += tx;
+          c.y += ty;
+          c.z += tz;
+          if constexpr (POT) c.w += tp;
+          js[k] = c;
+          asm volatile("" ::: "memory");
+          y = yn;
+        }
+      }
+      // j-side sums of this sweep: add the W waves in ascending order
+      __syncthreads();
+      for (int e = tid; e < NC * kWave; e += W * kWave) {
+        const int c = e / kWave, l = e % kWave;
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+          const float *sw = reinterpret_cast<const float *>(jsum + w * 2 * kWave);
+          sum += sw[4 * l + c] + sw[4 * (l + kWave) + c];
+        }
+        // the force on j from i points the other way; the potential does not
+        part[(((size_t)J * P + I) * NC + c) * B + g * kWave + l] = c < 3 ? -sum : sum;
+      }
+      __syncthreads();
+    }
+  } else {
   for (int g = 0; g < NG; ++g) {
     float xj[KP], yj[KP], zj[KP], mj[KP], cx[KP], cy[KP], cz[KP], cp[KP];
 #pragma unroll
@@ -210,6 +297,7 @@ __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, i
       __syncthreads();
     }
   }
+  }
 
 #pragma unroll
   for (int q = 0; q < K; ++q) {
@@ -224,20 +312,25 @@ __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, i
 
 // One block per task (panel pair); PanelOrder gives the pair of each block
 // (every XCD walks a contiguous stretch of tile-ordered pairs).
-template <int K, int KP, int W, int OCC, int IL, bool POT, int ML>
+template <int K, int KP, int W, int OCC, int IL, bool POT, int ML, int JL>
 __global__ __launch_bounds__(W *kWave) __attribute__((amdgpu_waves_per_eu(OCC))) void
 symmetric_task_kernel(const float4 *__restrict__ pm, int n, PanelOrder order, float eps2,
                       float *__restrict__ part) {
-  __shared__ float csum[W][KP][sym_sums<POT>()][kWave];
+  constexpr int NC = sym_sums<POT>();
+  __shared__ float csum[JL > 0 ? 1 : W][KP][NC][kWave];
   __shared__ float mis[ML > 0 ? W * ML * kWave : 1];
+  __shared__ float4 jtile[JL > 0 ? W * 2 * kWave : 1];
+  __shared__ float4 jsum[JL > 0 ? W * 2 * kWave : 1];
   int Ic, Jc;
   long long t;
   if (!panel_pair_of_block(order, blockIdx.x, Ic, Jc, t)) return;  // whole block: no barrier skipped
   const int P = order.P;
   if (Ic == Jc)
-    sym_task<K, KP, W, IL, POT, ML, true>(pm, n, Ic, Jc, P, eps2, part, csum, mis);
+    sym_task<K, KP, W, IL, POT, ML, JL, true>(pm, n, Ic, Jc, P, eps2, part, csum, mis, jtile,
+                                              jsum);
   else
-    sym_task<K, KP, W, IL, POT, ML, false>(pm, n, Ic, Jc, P, eps2, part, csum, mis);
+    sym_task<K, KP, W, IL, POT, ML, JL, false>(pm, n, Ic, Jc, P, eps2, part, csum, mis, jtile,
+                                               jsum);
 }
 
 // a_i = G sum_J part[I][J][c][b] over J ascending; with POT the fourth sum is
@@ -261,56 +354,72 @@ __global__ __launch_bounds__(256) void symmetric_reduce_kernel(const float *__re
   out[i] = make_float4(G * sx, G * sy, G * sz, POT ? -G * sp : 0.0f);
 }
 
-// (id, K, KP, waves, occupancy target, interleave width, i-masses in LDS);
-// panel B = 64 * waves * K.  Interleave widths 2 and 4 (variants 12, 13)
-// measured the same as 1 on MI355X: under the 6-waves-per-SIMD register
+// (id, K, KP, waves, occupancy target, interleave width, i-masses in LDS,
+// JL: 0 = rotated j-state, else LDS-carried with JL steps per unrolled
+// block); panel B = 64 * waves * K.  Interleave widths 2 and 4 (variants 12,
+// 13) measured the same as 1 on MI355X: under the 6-waves-per-SIMD register
 // budget the compiler schedules the pairs one after the other either way.
 // Variant 14 keeps 5 of its 8 i-masses in LDS (read once per pair inside the
 // step), which lets K = 8 fit 72 VGPRs without spilling: 7 waves per SIMD
 // instead of 6, and 193 against 206 ms at 2^20 bodies.  Asking for 8 waves
 // instead (64 VGPRs) makes the compiler spill to scratch inside the step
-// loop: 197 ms, and ~9 GB more memory traffic per pass.
+// loop: 197 ms, and ~9 GB more memory traffic per pass.  Variant 15 is 14
+// with the j-state carried in LDS (7 waves; a few spills outside the step
+// loop): 181 against 195 ms for variant 14 on the same box; 16 (i-masses in
+// registers, 6 waves) and 18 (six i-masses in LDS) measured 1-3 % slower.
+// Variant 17 is its 1024-body-panel form, for n up to ~2e5 (3.3 against
+// 3.6 ms for variant 8 at 131072 bodies).
 #define NBODY_SYM_VARIANTS(X) \
-  X(0, 8, 2, 4, 4, 1, 0)        \
-  X(1, 8, 1, 4, 4, 1, 0)        \
-  X(2, 4, 2, 4, 6, 1, 0)        \
-  X(3, 8, 2, 8, 4, 1, 0)        \
-  X(4, 4, 4, 4, 4, 1, 0)        \
-  X(5, 8, 1, 8, 4, 1, 0)        \
-  X(6, 16, 1, 4, 2, 1, 0)       \
-  X(7, 12, 1, 4, 3, 1, 0)       \
-  X(8, 8, 1, 2, 4, 1, 0)        \
-  X(9, 8, 1, 4, 6, 1, 0)        \
-  X(10, 6, 1, 4, 5, 1, 0)       \
-  X(11, 16, 1, 2, 2, 1, 0)      \
-  X(12, 8, 1, 4, 6, 4, 0)       \
-  X(13, 8, 1, 4, 6, 2, 0)       \
-  X(14, 8, 1, 4, 7, 1, 5)
+  X(0, 8, 2, 4, 4, 1, 0, 0)     \
+  X(1, 8, 1, 4, 4, 1, 0, 0)     \
+  X(2, 4, 2, 4, 6, 1, 0, 0)     \
+  X(3, 8, 2, 8, 4, 1, 0, 0)     \
+  X(4, 4, 4, 4, 4, 1, 0, 0)     \
+  X(5, 8, 1, 8, 4, 1, 0, 0)     \
+  X(6, 16, 1, 4, 2, 1, 0, 0)    \
+  X(7, 12, 1, 4, 3, 1, 0, 0)    \
+  X(8, 8, 1, 2, 4, 1, 0, 0)     \
+  X(9, 8, 1, 4, 6, 1, 0, 0)     \
+  X(10, 6, 1, 4, 5, 1, 0, 0)    \
+  X(11, 16, 1, 2, 2, 1, 0, 0)   \
+  X(12, 8, 1, 4, 6, 4, 0, 0)    \
+  X(13, 8, 1, 4, 6, 2, 0, 0)    \
+  X(14, 8, 1, 4, 7, 1, 5, 0)    \
+  X(15, 8, 1, 4, 7, 1, 5, 8)    \
+  X(16, 8, 1, 4, 6, 1, 0, 8)    \
+  X(17, 8, 1, 2, 7, 1, 5, 8)    \
+  X(18, 8, 1, 4, 7, 1, 6, 8)
 
 // Variants of the pass that also sums the potential (id, K, KP, waves,
-// occupancy target, i-masses in LDS); the ids are their own
+// occupancy target, i-masses in LDS, JL as above); the ids are their own
 // (nbody_accel_symmetric_potential).  The potential sums take K = 8 to ~96
 // VGPRs (5 waves per SIMD, variant 3: 266 ms at 2^20 bodies); capping it at
 // 80 (6 waves) leaves a few spills outside the step loop and, with 2 of the
-// i-masses in LDS, takes 216 ms (variant 1).
+// i-masses in LDS, takes 216 ms (variant 1).  With the j-state in LDS,
+// 5 waves and 4 i-masses in LDS (variant 6, no spills) it takes 203 ms;
+// variant 7 is its 1024-body-panel form.
 #define NBODY_SYM_POT_VARIANTS(X) \
-  X(0, 8, 1, 2, 6, 0)             \
-  X(1, 8, 1, 4, 6, 2)             \
-  X(2, 6, 1, 4, 6, 0)             \
-  X(3, 8, 1, 4, 5, 0)
+  X(0, 8, 1, 2, 6, 0, 0)          \
+  X(1, 8, 1, 4, 6, 2, 0)          \
+  X(2, 6, 1, 4, 6, 0, 0)          \
+  X(3, 8, 1, 4, 5, 0, 0)          \
+  X(4, 8, 1, 4, 6, 6, 8)          \
+  X(5, 8, 1, 4, 5, 8, 8)          \
+  X(6, 8, 1, 4, 5, 4, 8)          \
+  X(7, 8, 1, 2, 5, 4, 8)
 
 struct SymVariant {
   int K, KP, W;
 };
 
 const SymVariant kSym[] = {
-#define X(id, K, KP, W, OCC, IL, ML) {K, KP, W},
+#define X(id, K, KP, W, OCC, IL, ML, JL) {K, KP, W},
     NBODY_SYM_VARIANTS(X)
 #undef X
 };
 
 const SymVariant kSymPot[] = {
-#define X(id, K, KP, W, OCC, ML) {K, KP, W},
+#define X(id, K, KP, W, OCC, ML, JL) {K, KP, W},
     NBODY_SYM_POT_VARIANTS(X)
 #undef X
 };
@@ -324,14 +433,15 @@ int symmetric_variant_count(bool pot) {
 }
 
 // Measured on MI355X (force-pass sweeps): 8 i-bodies and 1 j-body per lane
-// is fastest from 1e5 bodies on; 1024-body panels (2-wave blocks) give more
-// panel pairs at the low end, 2048-body panels at 7 waves per SIMD are
-// fastest from ~2e5 bodies and halve the workspace.  Below ~5e4 bodies there are too few panel pairs
-// to fill the chip and the one-sided nbody_accel is faster.  The potential
-// variants follow the same split by n.
+// with the j-state in LDS is fastest from 1e5 bodies on; 1024-body panels
+// (2-wave blocks) give more panel pairs at the low end, 2048-body panels are
+// fastest from ~2e5 bodies and halve the workspace.  Below ~5e4 bodies there
+// are too few panel pairs to fill the chip and the one-sided nbody_accel is
+// faster.  The potential variants follow the same split by n, with the same
+// panel shapes and j-state carriage, so their xyz equal the plain pass's.
 int symmetric_variant_for_n(int64_t n, bool pot) {
-  if (pot) return n <= 200000 ? 0 : 1;
-  return n <= 200000 ? 8 : 14;
+  if (pot) return n <= 200000 ? 7 : 6;
+  return n <= 200000 ? 17 : 15;
 }
 
 int symmetric_panel(int v, bool pot) {
@@ -360,9 +470,9 @@ hipError_t launch_symmetric(const float *posmass, int n, float G, float eps2, fl
   const float4 *pm = reinterpret_cast<const float4 *>(posmass);
   if (!pot) {
     switch (v) {
-#define X(id, K, KP, W, OCC, IL, ML)                                                   \
+#define X(id, K, KP, W, OCC, IL, ML, JL)                                               \
   case id:                                                                             \
-    hipLaunchKernelGGL((symmetric_task_kernel<K, KP, W, OCC, IL, false, ML>),          \
+    hipLaunchKernelGGL((symmetric_task_kernel<K, KP, W, OCC, IL, false, ML, JL>),      \
                        dim3((unsigned)blocks), dim3(W * kWave), 0, stream, pm, n, order, eps2, \
                        part);                                                          \
     break;
@@ -373,9 +483,9 @@ hipError_t launch_symmetric(const float *posmass, int n, float G, float eps2, fl
     }
   } else {
     switch (v) {
-#define X(id, K, KP, W, OCC, ML)                                                       \
+#define X(id, K, KP, W, OCC, ML, JL)                                                   \
   case id:                                                                             \
-    hipLaunchKernelGGL((symmetric_task_kernel<K, KP, W, OCC, 1, true, ML>),            \
+    hipLaunchKernelGGL((symmetric_task_kernel<K, KP, W, OCC, 1, true, ML, JL>),        \
                        dim3((unsigned)blocks), dim3(W * kWave), 0, stream, pm, n, order, eps2, \
                        part);                                                          \
     break;

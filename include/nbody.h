@@ -188,14 +188,18 @@ size_t nbody_accel_splitj_tree_workspace_bytes(int64_t n, int64_t j_chunk, int t
 /* Pair-symmetric force pass: each unordered pair is evaluated once and its
  * term is applied to both bodies (Newton's third law).  The atomics tutorial
  * ("CUDA programming (9)", neighbour-list example) runs this symmetric half
- * loop with atomicAdd for the second body; here the second body's share is
- * carried in registers, rotated across the wavefront, and every sum has a
- * fixed order, so the result is bitwise reproducible.  Bodies are grouped in
+ * loop with atomicAdd for the second body; here no atomics are used: the
+ * second body's share is carried either in registers rotated across the
+ * wavefront or in a per-wave LDS slot that one lane at a time reads, adds to
+ * and writes back, and every sum has a fixed order, so the result is bitwise
+ * reproducible for a given (n, variant).  Bodies are grouped in
  * panels of nbody_accel_symmetric_panel(variant) bodies; a panel pair (I, J)
  * writes panel I's sums from J and panel J's sums from I into the
  * workspace, and a second kernel adds, for each body, the P panel sums in
  * ascending panel order and multiplies by G.  The order differs from
- * nbody_accel's, so the two agree to rounding, not bitwise.
+ * nbody_accel's, so the two agree to rounding, not bitwise; variants that
+ * carry the second body's share differently (registers or LDS) also agree
+ * to rounding only.
  *   variant    0 <= variant < nbody_accel_symmetric_variant_count(), or -1
  *              for the library's choice.
  *   workspace  >= nbody_accel_symmetric_workspace_bytes(n, variant) bytes

@@ -420,6 +420,23 @@ def test_symmetric_interleave_variants_bitwise_equal():
         assert np.array_equal(sym_accel(pm, eps2=1e-5, variant=v), base), v
 
 
+def test_symmetric_lds_carried_variants_bitwise_equal():
+    """The variants that keep the j-state in LDS (15, 16, 18) differ only in
+    how many i-masses sit in LDS and in occupancy: the same sums, bitwise.
+    Against the lane-rotating variant of the same panel (9) only the j-side
+    order differs, so they agree to rounding."""
+    pm, _ = workloads.uniform_cube(6000, seed=56, masses="lognormal")
+    base = sym_accel(pm, eps2=1e-5, variant=15)
+    for v in (16, 18):
+        assert nb.nbody_accel_symmetric_panel(v) == nb.nbody_accel_symmetric_panel(15)
+        assert np.array_equal(sym_accel(pm, eps2=1e-5, variant=v), base), v
+    rot = sym_accel(pm, eps2=1e-5, variant=9).astype(np.float64)
+    ref = ref_accel(pm, eps2=1e-5)
+    assert_parity(base, ref, "symmetric v15 n=6000")
+    d = np.linalg.norm(base[:, :3] - rot[:, :3]) / np.linalg.norm(ref[:, :3])
+    assert d <= 1e-6, d
+
+
 # ---------------------------------------------------------------------------
 # Degenerate inputs
 # ---------------------------------------------------------------------------
