@@ -436,12 +436,14 @@ int symmetric_variant_count(bool pot) {
 // with the j-state in LDS is fastest from 1e5 bodies on; 1024-body panels
 // (2-wave blocks) give more panel pairs at the low end, 2048-body panels are
 // fastest from ~2e5 bodies and halve the workspace.  Below ~5e4 bodies there
-// are too few panel pairs to fill the chip and the one-sided nbody_accel is
-// faster.  The potential variants follow the same split by n, with the same
+// are too few panel pairs to fill the chip: each task's latency counts, and
+// the rotated state, with no LDS round trip per step, is faster (0.30
+// against 0.43 ms at 16384 bodies); the one-sided nbody_accel is faster
+// still.  The potential variants follow the same split by n, with the same
 // panel shapes and j-state carriage, so their xyz equal the plain pass's.
 int symmetric_variant_for_n(int64_t n, bool pot) {
-  if (pot) return n <= 200000 ? 7 : 6;
-  return n <= 200000 ? 17 : 15;
+  if (pot) return n <= 50000 ? 0 : n <= 200000 ? 7 : 6;
+  return n <= 50000 ? 8 : n <= 200000 ? 17 : 15;
 }
 
 int symmetric_panel(int v, bool pot) {
