@@ -367,8 +367,9 @@ __global__ __launch_bounds__(256) void symmetric_reduce_kernel(const float *__re
 // with the j-state carried in LDS (7 waves; a few spills outside the step
 // loop): 181 against 195 ms for variant 14 on the same box; 16 (i-masses in
 // registers, 6 waves) and 18 (six i-masses in LDS) measured 1-3 % slower.
-// Variant 17 is its 1024-body-panel form, for n up to ~2e5 (3.3 against
-// 3.6 ms for variant 8 at 131072 bodies).
+// Variant 17 is its 1024-body-panel form.  With the j-state in LDS the
+// per-pair cost of a small K is low, so K = 4 (20: 64 VGPRs, 8 waves per
+// SIMD, no spills) and K = 2 (19) serve the smaller sizes.
 #define NBODY_SYM_VARIANTS(X) \
   X(0, 8, 2, 4, 4, 1, 0, 0)     \
   X(1, 8, 1, 4, 4, 1, 0, 0)     \
@@ -388,7 +389,9 @@ __global__ __launch_bounds__(256) void symmetric_reduce_kernel(const float *__re
   X(15, 8, 1, 4, 7, 1, 5, 8)    \
   X(16, 8, 1, 4, 6, 1, 0, 8)    \
   X(17, 8, 1, 2, 7, 1, 5, 8)    \
-  X(18, 8, 1, 4, 7, 1, 6, 8)
+  X(18, 8, 1, 4, 7, 1, 6, 8)    \
+  X(19, 2, 1, 2, 8, 1, 0, 8)    \
+  X(20, 4, 1, 4, 8, 1, 0, 8)
 
 // Variants of the pass that also sums the potential (id, K, KP, waves,
 // occupancy target, i-masses in LDS, JL as above); the ids are their own
@@ -396,8 +399,9 @@ __global__ __launch_bounds__(256) void symmetric_reduce_kernel(const float *__re
 // VGPRs (5 waves per SIMD, variant 3: 266 ms at 2^20 bodies); capping it at
 // 80 (6 waves) leaves a few spills outside the step loop and, with 2 of the
 // i-masses in LDS, takes 216 ms (variant 1).  With the j-state in LDS,
-// 5 waves and 4 i-masses in LDS (variant 6, no spills) it takes 203 ms;
-// variant 7 is its 1024-body-panel form.
+// 5 waves and 4 i-masses in LDS (variant 6, no spills) it takes 203 ms.
+// Variants 7, 8 and 9 are 1024-body (K = 8 and K = 4) and 256-body panel
+// forms; 8 and 9 share the shapes of the plain variants 20 and 19.
 #define NBODY_SYM_POT_VARIANTS(X) \
   X(0, 8, 1, 2, 6, 0, 0)          \
   X(1, 8, 1, 4, 6, 2, 0)          \
@@ -406,7 +410,9 @@ __global__ __launch_bounds__(256) void symmetric_reduce_kernel(const float *__re
   X(4, 8, 1, 4, 6, 6, 8)          \
   X(5, 8, 1, 4, 5, 8, 8)          \
   X(6, 8, 1, 4, 5, 4, 8)          \
-  X(7, 8, 1, 2, 5, 4, 8)
+  X(7, 8, 1, 2, 5, 4, 8)          \
+  X(8, 4, 1, 4, 8, 0, 8)          \
+  X(9, 2, 1, 2, 8, 0, 8)
 
 struct SymVariant {
   int K, KP, W;
@@ -432,18 +438,20 @@ int symmetric_variant_count(bool pot) {
   return pot ? (int)(sizeof(kSymPot) / sizeof(kSymPot[0])) : (int)(sizeof(kSym) / sizeof(kSym[0]));
 }
 
-// Measured on MI355X (force-pass sweeps): 8 i-bodies and 1 j-body per lane
-// with the j-state in LDS is fastest from 1e5 bodies on; 1024-body panels
-// (2-wave blocks) give more panel pairs at the low end, 2048-body panels are
-// fastest from ~2e5 bodies and halve the workspace.  Below ~5e4 bodies there
-// are too few panel pairs to fill the chip: each task's latency counts, and
-// the rotated state, with no LDS round trip per step, is faster (0.30
-// against 0.43 ms at 16384 bodies); the one-sided nbody_accel is faster
-// still.  The potential variants follow the same split by n, with the same
-// panel shapes and j-state carriage, so their xyz equal the plain pass's.
+// Measured on MI355X (force-pass sweeps), all with the j-state in LDS: 8
+// i-bodies per lane in 2048-body panels at 7 waves per SIMD (15) from ~2.5e5
+// bodies on (45.6 ms at 2^19 bodies, against 47.5 ms for 20); 4 i-bodies per
+// lane in 1024-body panels at 8 waves (20) from ~3e4 to ~2.5e5 (0.89 ms at
+// 65536 bodies, 3.17 ms at 131072, against 1.10 and 3.37 ms for 17); 2
+// i-bodies per lane in 256-body panels (19) below that, where larger panels
+// leave too few panel pairs to fill the chip (0.107 ms at 16384 bodies,
+// against 0.30 ms for the rotated 8; the one-sided nbody_accel takes 0.10
+// ms there).  The potential variants follow the same split by n, with the
+// same panel shapes and j-state carriage, so their xyz equal the plain
+// pass's.
 int symmetric_variant_for_n(int64_t n, bool pot) {
-  if (pot) return n <= 50000 ? 0 : n <= 200000 ? 7 : 6;
-  return n <= 50000 ? 8 : n <= 200000 ? 17 : 15;
+  if (pot) return n <= 32768 ? 9 : n <= 200000 ? 8 : 6;
+  return n <= 32768 ? 19 : n <= 200000 ? 20 : 15;
 }
 
 int symmetric_panel(int v, bool pot) {

@@ -455,7 +455,10 @@ def test_empty_input_is_a_no_op():
     assert stats.cpu().tolist() == [7.0] * 8     # n == 0 touches nothing
 
 
+# symmetric_lds: the LDS-carried j-state with 1024-body panels, so that the
+# small cases below have off-diagonal panel pairs
 PATHS = {"tile": lambda pm, *a: gpu_accel(pm, *a), "symmetric": lambda pm, *a: sym_accel(pm, *a),
+         "symmetric_lds": lambda pm, *a: sym_accel(pm, *a, variant=17),
          "splitj_tree": lambda pm, *a: tree_accel(pm, *a)}
 
 
