@@ -10,13 +10,15 @@
 //     atomic tail).  The same kernel with the potential flag takes
 //     W_i = m_i Phi_i / 2 from accel.w (nbody_energy_from_potential).
 //  2. energy_pairs_kernel: the pair sum of W over panel-pair tasks (I <= J),
-//     the rotation scheme of the pair-symmetric force pass: each lane keeps K
-//     i-bodies, a j-body rotates one lane per step, every unordered pair is
-//     met once (in a diagonal task, twice, and halved; the j = i pair is the
-//     step-0 pair of the lane's own sweep and is skipped).  Per (lane, i-body)
-//     the terms m_j / sqrt(r^2 + eps^2) of a 64-step sweep are summed in fp32,
-//     multiplied by m_i and added in fp64; lanes are added in a fixed tree.
-//     One fp64 value per task.
+//     the panel-pair scheme of the pair-symmetric force pass: each lane keeps
+//     K i-bodies, every unordered pair is met once (in a diagonal task,
+//     twice, and halved; the j = i pair is skipped by an index test).  The
+//     pair potential is symmetric, so no j-side sum is needed: each wave
+//     stages 64 j-bodies in its LDS tile and all lanes read the same one per
+//     step (a broadcast read, no lane rotation).  Per (lane, i-body) the
+//     terms m_j / sqrt(r^2 + eps^2) of a 64-body sweep are summed in fp32 in
+//     ascending j, multiplied by m_i and added in fp64; lanes are added in a
+//     fixed tree.  One fp64 value per task.
 //  3. energy_final_kernel: block sums and task sums in fixed orders.
 #include "nbody_common.hpp"
 #include "nbody_internal.hpp"
@@ -66,8 +68,9 @@ __global__ __launch_bounds__(kBodyThreads) void energy_bodies_kernel(
 
 template <bool DIAG>
 __device__ __forceinline__ double pair_potential_task(const float4 *__restrict__ pm, int n, int I,
-                                                      int J, float eps2) {
+                                                      int J, float eps2, float4 *jt) {
   constexpr int K = kPairK, B = kPairPanel, NG = B / kWave;
+  constexpr int U = 2;  // steps per unrolled block (more spills at 8 waves per SIMD)
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
@@ -85,25 +88,29 @@ __device__ __forceinline__ double pair_potential_task(const float4 *__restrict__
   for (int g = 0; g < NG; ++g) {
     const int j = J * B + g * kWave + lane;
     const float4 b = pm[j < n ? j : n - 1];
-    float xj = b.x, yj = b.y, zj = b.z, mj = j < n ? b.w : 0.0f;
+    jt[lane] = make_float4(b.x, b.y, b.z, j < n ? b.w : 0.0f);
+    // every lane reads what the others wrote: keep the LDS accesses on
+    // their side of this point (one wave's LDS instructions run in order)
+    asm volatile("" ::: "memory");
     float s[K];
 #pragma unroll
     for (int q = 0; q < K; ++q) s[q] = 0.0f;
-    for (int step = 0; step < kWave; ++step) {
+    for (int s0 = 0; s0 < kWave; s0 += U) {
 #pragma unroll
-      for (int q = 0; q < K; ++q) {
-        const float inv = pair_rsq(xj, yj, zj, xi[q], yi[q], zi[q], eps2);
-        float mp = mj;
-        // in a diagonal task lane l meets its own body at step 0 of the
-        // sweep whose j-group is that body's group (wave * K + q)
-        if constexpr (DIAG) mp = (step == 0 && g == wave * K + q) ? 0.0f : mj;
-        s[q] = __builtin_fmaf(mp, inv, s[q]);
+      for (int u = 0; u < U; ++u) {
+        const float4 y = jt[s0 + u];  // the same j-body for all lanes (broadcast)
+#pragma unroll
+        for (int q = 0; q < K; ++q) {
+          const float inv = pair_rsq(y.x, y.y, y.z, xi[q], yi[q], zi[q], eps2);
+          float mp = y.w;
+          // in a diagonal task lane l meets its own body at step l of the
+          // sweep whose j-group is that body's group (wave * K + q)
+          if constexpr (DIAG) mp = (g == wave * K + q && s0 + u == lane) ? 0.0f : y.w;
+          s[q] = __builtin_fmaf(mp, inv, s[q]);
+        }
       }
-      xj = rotate_lanes(xj);
-      yj = rotate_lanes(yj);
-      zj = rotate_lanes(zj);
-      mj = rotate_lanes(mj);
     }
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int q = 0; q < K; ++q) acc += (double)mi[q] * (double)s[q];
   }
@@ -113,16 +120,19 @@ __device__ __forceinline__ double pair_potential_task(const float4 *__restrict__
 // One block per panel pair (I, J), I <= J, in the XCD-aware order of
 // PanelOrder: task_out[t] = sum over the pairs of m_i m_j / sqrt(r^2 + eps^2),
 // each unordered pair once, t the pair's number in that order.
-__global__ __launch_bounds__(kPairW *kWave) void energy_pairs_kernel(
+__global__ __launch_bounds__(kPairW *kWave) __attribute__((amdgpu_waves_per_eu(8))) void
+energy_pairs_kernel(
     const float4 *__restrict__ pm, int n, PanelOrder order, float eps2,
     double *__restrict__ task_out) {
   __shared__ double red[kPairW * kWave];
+  __shared__ float4 jtile[kPairW * kWave];  // one 64-body j-tile per wave
   int I, J;
   long long t;
   if (!panel_pair_of_block(order, blockIdx.x, I, J, t)) return;  // whole block: no barrier skipped
-  double acc = I == J ? pair_potential_task<true>(pm, n, I, J, eps2)
-                      : pair_potential_task<false>(pm, n, I, J, eps2);
   const int tid = threadIdx.x;
+  float4 *jt = jtile + (tid / kWave) * kWave;
+  double acc = I == J ? pair_potential_task<true>(pm, n, I, J, eps2, jt)
+                      : pair_potential_task<false>(pm, n, I, J, eps2, jt);
   red[tid] = acc;
   __syncthreads();
   for (int s = kPairW * kWave / 2; s > 0; s >>= 1) {
