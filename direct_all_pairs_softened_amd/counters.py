@@ -75,6 +75,14 @@ def cmd_run(args):
     torch.cuda.synchronize()
     pm = torch.from_numpy(pm_np).to(dev)
     acc = torch.empty_like(pm)
+    if args.path == "energy":
+        vel = torch.from_numpy(workloads.make(w.name)[1]).to(dev)
+        ws = torch.empty(nb.nbody_energy_workspace_bytes(w.n), dtype=torch.uint8, device=dev)
+        stats = torch.zeros(8, dtype=torch.float64, device=dev)
+        nb.nbody_energy(pm, vel, w.G, w.eps2, ws, stats)
+        torch.cuda.synchronize()
+        print(f"counters run: copy {COPY_BYTES} B, energy on {w.name}", flush=True)
+        return
     if args.path == "symmetric":
         v = args.variant if args.variant is not None else nb.nbody_accel_symmetric_variant_for_n(w.n)
         ws = torch.empty(nb.nbody_accel_symmetric_workspace_bytes(w.n, v), dtype=torch.uint8,
@@ -86,6 +94,32 @@ def cmd_run(args):
     torch.cuda.synchronize()
     print(f"counters run: copy {COPY_BYTES} B, {args.path} force variant {v} on {w.name}",
           flush=True)
+
+
+def cmd_sq_report(args):
+    """Prints the SQ/GRBM counters of the first dispatch of a kernel and the
+    rates derived from them (MI355X: 8 XCDs, 256 CUs, 4 SIMDs per CU)."""
+    c = read_counters(os.path.join(args.dir, "**", "*counter_collection.csv"))
+    name, v = pick(c, (args.kernel,))
+    print(f"kernel: `{name}`")
+    print("")
+    print("| counter | value |")
+    print("|---|---|")
+    for k in sorted(v):
+        print(f"| {k} | {v[k]:.4e} |")
+    print("")
+    g = v.get("GRBM_GUI_ACTIVE", 0.0) / 8
+    if g:
+        print(f"- cycles per XCD (GRBM_GUI_ACTIVE / 8): {g:.4e}")
+        if args.ms:
+            print(f"- clock over {args.ms:.2f} ms: {g / (args.ms * 1e-3) / 1e9:.2f} GHz")
+        if "SQ_INSTS_VALU" in v:
+            print(f"- VALU instructions per SIMD quad-cycle: {v['SQ_INSTS_VALU'] / 1024 / (g / 4):.3f}")
+        if "SQ_ACTIVE_INST_VALU2" in v:
+            print(f"- quad-cycles issuing two VALU instructions: "
+                  f"{100 * v['SQ_ACTIVE_INST_VALU2'] / (g * 256):.1f} %")
+        if "SQ_BUSY_CU_CYCLES" in v:
+            print(f"- SIMD quad-cycles busy: {100 * v['SQ_BUSY_CU_CYCLES'] / (g * 256):.1f} %")
 
 
 def read_counters(pattern):
@@ -243,7 +277,12 @@ def main():
     r = sub.add_parser("run")
     r.add_argument("--workload", default="plummer1m")
     r.add_argument("--variant", type=int, default=None)
-    r.add_argument("--path", choices=("tile", "symmetric"), default="symmetric")
+    r.add_argument("--path", choices=("tile", "symmetric", "energy"), default="symmetric")
+    q = sub.add_parser("sq-report", help="SQ/GRBM counters of one kernel, with derived rates")
+    q.add_argument("--dir", required=True)
+    q.add_argument("--kernel", required=True, help="a substring of the kernel name")
+    q.add_argument("--ms", type=float, default=None,
+                   help="the kernel's traced duration, for the clock estimate")
     s = sub.add_parser("summarize")
     s.add_argument("--fetch-dir", required=True)
     s.add_argument("--write-dir", required=True)
@@ -268,6 +307,7 @@ def main():
                         "second passes that follow first passes of different shapes)")
     a = ap.parse_args()
     {"run": cmd_run, "summarize": cmd_summarize, "trace-report": cmd_trace_report,
+     "sq-report": cmd_sq_report,
      "dispatch-report": cmd_dispatch_report}[a.cmd](a)
 
 

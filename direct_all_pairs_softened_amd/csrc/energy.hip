@@ -70,7 +70,7 @@ template <bool DIAG>
 __device__ __forceinline__ double pair_potential_task(const float4 *__restrict__ pm, int n, int I,
                                                       int J, float eps2, float4 *jt) {
   constexpr int K = kPairK, B = kPairPanel, NG = B / kWave;
-  constexpr int U = 2;  // steps per unrolled block (more spills at 8 waves per SIMD)
+  constexpr int U = 2;  // steps per unrolled block
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
@@ -99,14 +99,31 @@ __device__ __forceinline__ double pair_potential_task(const float4 *__restrict__
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const float4 y = jt[s0 + u];  // the same j-body for all lanes (broadcast)
+        // the K pairs of the step in phases (all differences, all d^2, all
+        // rsq, then the sums): K independent chains to issue from, where one
+        // pair after the other leaves the VALU waiting on each result
+        float dx[K], dy[K], dz[K], w[K];
 #pragma unroll
         for (int q = 0; q < K; ++q) {
-          const float inv = pair_rsq(y.x, y.y, y.z, xi[q], yi[q], zi[q], eps2);
+          dx[q] = y.x - xi[q];
+          dy[q] = y.y - yi[q];
+          dz[q] = y.z - zi[q];
+        }
+#pragma unroll
+        for (int q = 0; q < K; ++q) w[q] = __builtin_fmaf(dx[q], dx[q], eps2);
+#pragma unroll
+        for (int q = 0; q < K; ++q) w[q] = __builtin_fmaf(dy[q], dy[q], w[q]);
+#pragma unroll
+        for (int q = 0; q < K; ++q) w[q] = __builtin_fmaf(dz[q], dz[q], w[q]);
+#pragma unroll
+        for (int q = 0; q < K; ++q) w[q] = __builtin_amdgcn_rsqf(w[q]);
+#pragma unroll
+        for (int q = 0; q < K; ++q) {
           float mp = y.w;
           // in a diagonal task lane l meets its own body at step l of the
           // sweep whose j-group is that body's group (wave * K + q)
           if constexpr (DIAG) mp = (g == wave * K + q && s0 + u == lane) ? 0.0f : y.w;
-          s[q] = __builtin_fmaf(mp, inv, s[q]);
+          s[q] = __builtin_fmaf(mp, w[q], s[q]);
         }
       }
     }
@@ -120,8 +137,7 @@ __device__ __forceinline__ double pair_potential_task(const float4 *__restrict__
 // One block per panel pair (I, J), I <= J, in the XCD-aware order of
 // PanelOrder: task_out[t] = sum over the pairs of m_i m_j / sqrt(r^2 + eps^2),
 // each unordered pair once, t the pair's number in that order.
-__global__ __launch_bounds__(kPairW *kWave) __attribute__((amdgpu_waves_per_eu(8))) void
-energy_pairs_kernel(
+__global__ __launch_bounds__(kPairW *kWave) void energy_pairs_kernel(
     const float4 *__restrict__ pm, int n, PanelOrder order, float eps2,
     double *__restrict__ task_out) {
   __shared__ double red[kPairW * kWave];

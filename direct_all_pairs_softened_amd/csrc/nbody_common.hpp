@@ -61,19 +61,6 @@ __device__ __forceinline__ void pair_accel_pot(float xj, float yj, float zj, flo
   pp = __builtin_fmaf(mp, inv, pp);
 }
 
-// (|r|^2 + eps^2)^{-1/2} for one pair: the potential term of the energy is
-// m_j times this, with the j = i term dropped by the caller's index test.
-__device__ __forceinline__ float pair_rsq(float xj, float yj, float zj, float xi, float yi,
-                                          float zi, float eps2) {
-  const float dx = xj - xi;
-  const float dy = yj - yi;
-  const float dz = zj - zi;
-  float d2 = __builtin_fmaf(dx, dx, eps2);
-  d2 = __builtin_fmaf(dy, dy, d2);
-  d2 = __builtin_fmaf(dz, dz, d2);
-  return __builtin_amdgcn_rsqf(d2);
-}
-
 // Lane l receives lane l - 1's value (lane 0 receives lane 63's): one step of
 // the rotation that carries a j-body around the wavefront (DPP wave_ror:1).
 __device__ __forceinline__ float rotate_lanes(float v) {
