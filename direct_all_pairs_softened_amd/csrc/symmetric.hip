@@ -50,7 +50,10 @@ namespace {
 // independent chains to issue from; IL = 1 is one pair after the other.  The
 // arithmetic of each pair, and its order of accumulation, do not depend on IL.
 // POT adds the potential sums: i gains m_j inv, j gains m_i inv (two more
-// multiply-adds per pair; the force arithmetic is unchanged).
+// multiply-adds per pair; the force arithmetic is unchanged).  The last ML of
+// the K i-masses are read from LDS (mil[r * 64], r = 0 .. ML - 1) instead of
+// registers.  FRESH starts the j-side sums at this step: the first pair's
+// term is stored, not added.
 template <int K, int IL, bool POT, int ML, bool FRESH = false>
 __device__ __forceinline__ void sym_step(const float (&xi)[K], const float (&yi)[K],
                                          const float (&zi)[K], const float (&mi)[K],
@@ -216,87 +219,87 @@ __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, i
       __syncthreads();
     }
   } else {
-  for (int g = 0; g < NG; ++g) {
-    float xj[KP], yj[KP], zj[KP], mj[KP], cx[KP], cy[KP], cz[KP], cp[KP];
-#pragma unroll
-    for (int p = 0; p < KP; ++p) {
-      const int j = J * B + g * JG + p * kWave + lane;
-      const float4 b = pm[j < n ? j : n - 1];
-      xj[p] = b.x;
-      yj[p] = b.y;
-      zj[p] = b.z;
-      mj[p] = j < n ? b.w : 0.0f;
-      cx[p] = 0.0f;
-      cy[p] = 0.0f;
-      cz[p] = 0.0f;
-      cp[p] = 0.0f;
-    }
-    for (int s = 0; s < kWave; ++s) {
+    for (int g = 0; g < NG; ++g) {
+      float xj[KP], yj[KP], zj[KP], mj[KP], cx[KP], cy[KP], cz[KP], cp[KP];
 #pragma unroll
       for (int p = 0; p < KP; ++p) {
-        if constexpr (!DIAG) {
-          // masses kept in LDS are read inside the step: the empty asm that
-          // claims to change the index stops the compiler from hoisting the
-          // reads out of the loop into registers
-          int mio = wave * ML * kWave + lane;
-          if constexpr (ML > 0) asm volatile("" : "+v"(mio));
-          sym_step<K, IL, POT, ML>(xi, yi, zi, mi, mis + mio, xj[p], yj[p], zj[p], mj[p], eps2,
-                                   ax, ay, az, ap, cx[p], cy[p], cz[p], cp[p]);
-        } else {
+        const int j = J * B + g * JG + p * kWave + lane;
+        const float4 b = pm[j < n ? j : n - 1];
+        xj[p] = b.x;
+        yj[p] = b.y;
+        zj[p] = b.z;
+        mj[p] = j < n ? b.w : 0.0f;
+        cx[p] = 0.0f;
+        cy[p] = 0.0f;
+        cz[p] = 0.0f;
+        cp[p] = 0.0f;
+      }
+      for (int s = 0; s < kWave; ++s) {
 #pragma unroll
-        for (int q = 0; q < K; ++q) {
-          const float dx = xj[p] - xi[q];
-          const float dy = yj[p] - yi[q];
-          const float dz = zj[p] - zi[q];
-          float d2 = __builtin_fmaf(dx, dx, eps2);
-          d2 = __builtin_fmaf(dy, dy, d2);
-          d2 = __builtin_fmaf(dz, dz, d2);
-          const float inv = __builtin_amdgcn_rsqf(d2);
-          const float sj = (mj[p] * inv) * (inv * inv);
-          ax[q] = __builtin_fmaf(sj, dx, ax[q]);
-          ay[q] = __builtin_fmaf(sj, dy, ay[q]);
-          az[q] = __builtin_fmaf(sj, dz, az[q]);
-          if constexpr (POT) {
-            // lane l meets its own body at step 0 of the sweep whose j-bodies
-            // are that body's group: the self term m_i / eps is left out
-            const bool self = s == 0 && g * KP + p == wave * K + q;
-            ap[q] = __builtin_fmaf(self ? 0.0f : mj[p], inv, ap[q]);
+        for (int p = 0; p < KP; ++p) {
+          if constexpr (!DIAG) {
+            // masses kept in LDS are read inside the step: the empty asm that
+            // claims to change the index stops the compiler from hoisting the
+            // reads out of the loop into registers
+            int mio = wave * ML * kWave + lane;
+            if constexpr (ML > 0) asm volatile("" : "+v"(mio));
+            sym_step<K, IL, POT, ML>(xi, yi, zi, mi, mis + mio, xj[p], yj[p], zj[p], mj[p], eps2,
+                                     ax, ay, az, ap, cx[p], cy[p], cz[p], cp[p]);
+          } else {
+#pragma unroll
+            for (int q = 0; q < K; ++q) {
+              const float dx = xj[p] - xi[q];
+              const float dy = yj[p] - yi[q];
+              const float dz = zj[p] - zi[q];
+              float d2 = __builtin_fmaf(dx, dx, eps2);
+              d2 = __builtin_fmaf(dy, dy, d2);
+              d2 = __builtin_fmaf(dz, dz, d2);
+              const float inv = __builtin_amdgcn_rsqf(d2);
+              const float sj = (mj[p] * inv) * (inv * inv);
+              ax[q] = __builtin_fmaf(sj, dx, ax[q]);
+              ay[q] = __builtin_fmaf(sj, dy, ay[q]);
+              az[q] = __builtin_fmaf(sj, dz, az[q]);
+              if constexpr (POT) {
+                // lane l meets its own body at step 0 of the sweep whose j-bodies
+                // are that body's group: the self term m_i / eps is left out
+                const bool self = s == 0 && g * KP + p == wave * K + q;
+                ap[q] = __builtin_fmaf(self ? 0.0f : mj[p], inv, ap[q]);
+              }
+            }
+          }
+          xj[p] = rotate_lanes(xj[p]);
+          yj[p] = rotate_lanes(yj[p]);
+          zj[p] = rotate_lanes(zj[p]);
+          mj[p] = rotate_lanes(mj[p]);
+          if constexpr (!DIAG) {
+            cx[p] = rotate_lanes(cx[p]);
+            cy[p] = rotate_lanes(cy[p]);
+            cz[p] = rotate_lanes(cz[p]);
+            if constexpr (POT) cp[p] = rotate_lanes(cp[p]);
           }
         }
+      }
+      if constexpr (!DIAG) {
+        // j-side sums of this sweep: add the W waves in ascending order
+#pragma unroll
+        for (int p = 0; p < KP; ++p) {
+          csum[wave][p][0][lane] = cx[p];
+          csum[wave][p][1][lane] = cy[p];
+          csum[wave][p][2][lane] = cz[p];
+          if constexpr (POT) csum[wave][p][3][lane] = cp[p];
         }
-        xj[p] = rotate_lanes(xj[p]);
-        yj[p] = rotate_lanes(yj[p]);
-        zj[p] = rotate_lanes(zj[p]);
-        mj[p] = rotate_lanes(mj[p]);
-        if constexpr (!DIAG) {
-          cx[p] = rotate_lanes(cx[p]);
-          cy[p] = rotate_lanes(cy[p]);
-          cz[p] = rotate_lanes(cz[p]);
-          if constexpr (POT) cp[p] = rotate_lanes(cp[p]);
+        __syncthreads();
+        for (int e = tid; e < KP * NC * kWave; e += W * kWave) {
+          const int p = e / (NC * kWave), c = (e / kWave) % NC, l = e % kWave;
+          float sum = 0.0f;
+#pragma unroll
+          for (int w = 0; w < W; ++w) sum += csum[w][p][c][l];
+          // the force on j from i points the other way; the potential does not
+          part[(((size_t)J * P + I) * NC + c) * B + g * JG + p * kWave + l] = c < 3 ? -sum : sum;
         }
+        __syncthreads();
       }
     }
-    if constexpr (!DIAG) {
-      // j-side sums of this sweep: add the W waves in ascending order
-#pragma unroll
-      for (int p = 0; p < KP; ++p) {
-        csum[wave][p][0][lane] = cx[p];
-        csum[wave][p][1][lane] = cy[p];
-        csum[wave][p][2][lane] = cz[p];
-        if constexpr (POT) csum[wave][p][3][lane] = cp[p];
-      }
-      __syncthreads();
-      for (int e = tid; e < KP * NC * kWave; e += W * kWave) {
-        const int p = e / (NC * kWave), c = (e / kWave) % NC, l = e % kWave;
-        float sum = 0.0f;
-#pragma unroll
-        for (int w = 0; w < W; ++w) sum += csum[w][p][c][l];
-        // the force on j from i points the other way; the potential does not
-        part[(((size_t)J * P + I) * NC + c) * B + g * JG + p * kWave + l] = c < 3 ? -sum : sum;
-      }
-      __syncthreads();
-    }
-  }
   }
 
 #pragma unroll
