@@ -352,6 +352,23 @@ def test_symmetric_plummer1m_sampled():
     assert_parity(a, gpu_accel(pm, w.G, w.eps2).astype(np.float64), "symmetric vs one-sided 1m")
 
 
+@pytest.mark.parametrize("n", [40000, 131072, 262144])
+def test_symmetric_default_variant_at_switch_sizes(n):
+    """The library's choice around its switches (2-, 4- and 8-body i-groups at
+    32768 and 200000 bodies): lognormal masses, sampled rows including the
+    first and last 64 against the oracle, every row against the one-sided
+    pass, and a repeat bitwise."""
+    pm, _ = workloads.uniform_cube(n, seed=300 + n % 97, masses="lognormal")
+    rows = sample_rows(n, 256, seed=9)
+    ref = ref_accel(pm, 1.0, 1e-4, rows)
+    a = sym_accel(pm)
+    log(f"symmetric n={n} variant {nb.nbody_accel_symmetric_variant_for_n(n)}")
+    assert np.all(a[:, 3] == 0)
+    assert_parity(a[rows], ref, f"symmetric default n={n}")
+    assert_parity(a, gpu_accel(pm).astype(np.float64), f"symmetric vs one-sided n={n}")
+    assert np.array_equal(a, sym_accel(pm))
+
+
 def test_symmetric_collision1m_ragged_sampled():
     w = workloads.WORKLOADS["collision1m"]
     pm, _ = workloads.make("collision1m")
