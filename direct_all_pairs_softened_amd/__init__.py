@@ -40,6 +40,7 @@ EXPORTS = (
     "nbody_accel_symmetric", "nbody_accel_symmetric_workspace_bytes",
     "nbody_accel_symmetric_variant_count", "nbody_accel_symmetric_panel",
     "nbody_accel_symmetric_variant_for_n",
+    "nbody_accel_symmetric_tasks", "nbody_accel_symmetric_reduce",
     "nbody_accel_symmetric_potential", "nbody_accel_symmetric_potential_workspace_bytes",
     "nbody_accel_symmetric_potential_variant_count", "nbody_accel_symmetric_potential_panel",
     "nbody_accel_symmetric_potential_variant_for_n",
@@ -96,6 +97,8 @@ def load_library(path: str | None = None):
         "nbody_accel_symmetric_variant_count": (c_int, []),
         "nbody_accel_symmetric_panel": (c_int, [c_int]),
         "nbody_accel_symmetric_variant_for_n": (c_int, [c_i64]),
+        "nbody_accel_symmetric_tasks": (c_int, [vp, c_i64, c_f, c_int, vp, c_sz, vp]),
+        "nbody_accel_symmetric_reduce": (c_int, [c_i64, c_f, vp, c_int, vp, c_sz, vp]),
         "nbody_accel_symmetric_potential": (c_int, [vp, c_i64, c_f, c_f, vp, c_int, vp, c_sz,
                                                     vp]),
         "nbody_accel_symmetric_potential_workspace_bytes": (c_sz, [c_i64, c_int]),
@@ -315,6 +318,31 @@ def nbody_accel_symmetric(posmass, G: float, eps2: float, accel_out, workspace,
                                                 _f32(accel_out, "accel_out", (4,)),
                                                 int(variant), ws, nbytes, _stream(stream)),
            "nbody_accel_symmetric")
+
+
+def nbody_accel_symmetric_tasks(posmass, eps2: float, workspace, variant: int = -1, stream=None):
+    """First phase of nbody_accel_symmetric: the panel-pair kernel (posmass ->
+    the panel sums in workspace)."""
+    n = _n_of(posmass)
+    ws = _dev(workspace, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load_library().nbody_accel_symmetric_tasks(_f32(posmass, "posmass", (4,)), n, eps2,
+                                                      int(variant), ws, nbytes, _stream(stream)),
+           "nbody_accel_symmetric_tasks")
+
+
+def nbody_accel_symmetric_reduce(n: int, G: float, accel_out, workspace, variant: int = -1,
+                                 stream=None):
+    """Second phase of nbody_accel_symmetric: the panel sums in workspace ->
+    accel_out (the same n, variant and workspace as the tasks call)."""
+    if _n_of(accel_out) != n:
+        raise ValueError("accel_out must have n rows")
+    ws = _dev(workspace, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load_library().nbody_accel_symmetric_reduce(int(n), G,
+                                                       _f32(accel_out, "accel_out", (4,)),
+                                                       int(variant), ws, nbytes, _stream(stream)),
+           "nbody_accel_symmetric_reduce")
 
 
 def nbody_accel_symmetric_potential_workspace_bytes(n: int, variant: int = -1) -> int:

@@ -246,10 +246,12 @@ static size_t sym_workspace_bytes(int64_t n, int variant, bool pot) {
   return nbody::symmetric_workspace_bytes(n, v, pot);
 }
 
-static int sym_pass(const float *posmass, int64_t n, float G, float eps2, float *accel_out,
-                    int variant, bool pot, void *workspace, size_t workspace_bytes,
-                    void *stream) {
-  const int v = sym_variant(variant, n, pot);
+// Checks shared by the pair-symmetric entry points.  A phase that does not
+// read posmass, or does not write accel_out, passes it as null with want_pm
+// or want_out false.  NBODY_OK with n == 0 means there is nothing to launch.
+static int sym_check(const float *posmass, int64_t n, float G, float eps2,
+                     const float *accel_out, int v, bool pot, const void *workspace,
+                     size_t workspace_bytes, bool want_pm, bool want_out) {
   if (!n_ok(n)) return NBODY_ERR_INVALID_ARG;
   if (int s = check_consts(G, eps2)) return s;
   if (v >= nbody::symmetric_variant_count(pot)) return NBODY_ERR_INVALID_ARG;
@@ -257,15 +259,28 @@ static int sym_pass(const float *posmass, int64_t n, float G, float eps2, float 
   const int64_t P = nbody::symmetric_panels(n, v, pot);
   // one block per panel pair, the grid rounded up to whole XCD stretches
   if (P * (P + 1) / 2 > INT32_MAX - 8) return NBODY_ERR_INVALID_ARG;
-  if (!posmass || !accel_out) return NBODY_ERR_INVALID_ARG;
-  if (!aligned(posmass, 16) || !aligned(accel_out, 16)) return NBODY_ERR_ALIGNMENT;
+  if ((want_pm && !posmass) || (want_out && !accel_out)) return NBODY_ERR_INVALID_ARG;
+  if ((want_pm && !aligned(posmass, 16)) || (want_out && !aligned(accel_out, 16)))
+    return NBODY_ERR_ALIGNMENT;
   const size_t need = nbody::symmetric_workspace_bytes(n, v, pot);
   if (!workspace || workspace_bytes < need) return NBODY_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return NBODY_ERR_ALIGNMENT;
   const size_t bytes = (size_t)n * 16;
-  if (overlap(posmass, bytes, accel_out, bytes) || overlap(workspace, need, posmass, bytes) ||
-      overlap(workspace, need, accel_out, bytes))
+  if ((want_pm && want_out && overlap(posmass, bytes, accel_out, bytes)) ||
+      (want_pm && overlap(workspace, need, posmass, bytes)) ||
+      (want_out && overlap(workspace, need, accel_out, bytes)))
     return NBODY_ERR_ALIAS;
+  return NBODY_OK;
+}
+
+static int sym_pass(const float *posmass, int64_t n, float G, float eps2, float *accel_out,
+                    int variant, bool pot, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+  const int v = sym_variant(variant, n, pot);
+  if (int s = sym_check(posmass, n, G, eps2, accel_out, v, pot, workspace, workspace_bytes, true,
+                        true))
+    return s;
+  if (n == 0) return NBODY_OK;
   return hip_status(nbody::launch_symmetric(posmass, (int)n, G, eps2, accel_out, v, pot,
                                             workspace, as_stream(stream)));
 }
@@ -291,6 +306,28 @@ int nbody_accel_symmetric(const float *posmass, int64_t n, float G, float eps2,
                           size_t workspace_bytes, void *stream) {
   return sym_pass(posmass, n, G, eps2, accel_out, variant, false, workspace, workspace_bytes,
                   stream);
+}
+
+int nbody_accel_symmetric_tasks(const float *posmass, int64_t n, float eps2, int variant,
+                                void *workspace, size_t workspace_bytes, void *stream) {
+  const int v = sym_variant(variant, n, false);
+  if (int s = sym_check(posmass, n, 1.0f, eps2, nullptr, v, false, workspace, workspace_bytes,
+                        true, false))
+    return s;
+  if (n == 0) return NBODY_OK;
+  return hip_status(nbody::launch_symmetric_tasks(posmass, (int)n, eps2, v, false, workspace,
+                                                  as_stream(stream)));
+}
+
+int nbody_accel_symmetric_reduce(int64_t n, float G, float *accel_out, int variant,
+                                 const void *workspace, size_t workspace_bytes, void *stream) {
+  const int v = sym_variant(variant, n, false);
+  if (int s = sym_check(nullptr, n, G, 1.0f, accel_out, v, false, workspace, workspace_bytes,
+                        false, true))
+    return s;
+  if (n == 0) return NBODY_OK;
+  return hip_status(nbody::launch_symmetric_reduce((int)n, G, accel_out, v, false, workspace,
+                                                   as_stream(stream)));
 }
 
 int nbody_accel_symmetric_potential_variant_count(void) {

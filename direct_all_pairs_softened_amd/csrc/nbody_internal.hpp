@@ -69,6 +69,12 @@ int64_t symmetric_panels(int64_t n, int v, bool pot);
 size_t symmetric_workspace_bytes(int64_t n, int v, bool pot);
 hipError_t launch_symmetric(const float *posmass, int n, float G, float eps2, float *accel,
                             int v, bool pot, void *workspace, hipStream_t stream);
+// The two kernels of launch_symmetric: the panel-pair tasks (posmass ->
+// workspace) and the reduce (workspace -> accel).
+hipError_t launch_symmetric_tasks(const float *posmass, int n, float eps2, int v, bool pot,
+                                  void *workspace, hipStream_t stream);
+hipError_t launch_symmetric_reduce(int n, float G, float *accel, int v, bool pot,
+                                   const void *workspace, hipStream_t stream);
 
 // Integrator.
 hipError_t launch_leapfrog(float *posmass, float *vel, const float *accel, float dt, int n,

@@ -473,9 +473,8 @@ size_t symmetric_workspace_bytes(int64_t n, int v, bool pot) {
   return (size_t)P * (size_t)P * (pot ? 4 : 3) * (size_t)B * sizeof(float);
 }
 
-hipError_t launch_symmetric(const float *posmass, int n, float G, float eps2, float *accel,
-                            int v, bool pot, void *workspace, hipStream_t stream) {
-  const int B = symmetric_panel(v, pot);
+hipError_t launch_symmetric_tasks(const float *posmass, int n, float eps2, int v, bool pot,
+                                  void *workspace, hipStream_t stream) {
   const int P = (int)symmetric_panels(n, v, pot);
   const PanelOrder order = panel_order(P);
   const long long blocks = kXcds * order.per_xcd;
@@ -508,8 +507,14 @@ hipError_t launch_symmetric(const float *posmass, int n, float G, float eps2, fl
         return hipErrorInvalidValue;
     }
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_symmetric_reduce(int n, float G, float *accel, int v, bool pot,
+                                   const void *workspace, hipStream_t stream) {
+  const int B = symmetric_panel(v, pot);
+  const int P = (int)symmetric_panels(n, v, pot);
+  const float *part = reinterpret_cast<const float *>(workspace);
   if (pot)
     hipLaunchKernelGGL(symmetric_reduce_kernel<true>, dim3((n + 255) / 256), dim3(256), 0, stream,
                        part, n, P, B, G, reinterpret_cast<float4 *>(accel));
@@ -517,6 +522,13 @@ hipError_t launch_symmetric(const float *posmass, int n, float G, float eps2, fl
     hipLaunchKernelGGL(symmetric_reduce_kernel<false>, dim3((n + 255) / 256), dim3(256), 0,
                        stream, part, n, P, B, G, reinterpret_cast<float4 *>(accel));
   return hipGetLastError();
+}
+
+hipError_t launch_symmetric(const float *posmass, int n, float G, float eps2, float *accel,
+                            int v, bool pot, void *workspace, hipStream_t stream) {
+  const hipError_t e = launch_symmetric_tasks(posmass, n, eps2, v, pot, workspace, stream);
+  if (e != hipSuccess) return e;
+  return launch_symmetric_reduce(n, G, accel, v, pot, workspace, stream);
 }
 
 }  // namespace nbody

@@ -221,6 +221,22 @@ int nbody_accel_symmetric_panel(int variant);
 /* The variant nbody_accel_symmetric uses for n when passed -1. */
 int nbody_accel_symmetric_variant_for_n(int64_t n);
 
+/* nbody_accel_symmetric in its two phases, for callers that schedule them
+ * themselves (other work between them, or timing the panel-pair kernel on
+ * its own).  nbody_accel_symmetric_tasks runs the panel-pair kernel: it reads
+ * posmass and writes every panel sum into the workspace.
+ * nbody_accel_symmetric_reduce runs the second kernel: it adds each body's
+ * panel sums in ascending panel order into accel_out, times G.  The reduce
+ * must be given the same n, variant and workspace, with the contents the
+ * tasks call left, on the same stream or one ordered after it; the pair
+ * then gives accel_out bitwise equal to nbody_accel_symmetric's.  Arguments,
+ * workspace size and errors as nbody_accel_symmetric, restricted to the
+ * arrays each phase touches (the tasks phase checks eps2, the reduce G). */
+int nbody_accel_symmetric_tasks(const float *posmass, int64_t n, float eps2, int variant,
+                                void *workspace, size_t workspace_bytes, void *stream);
+int nbody_accel_symmetric_reduce(int64_t n, float G, float *accel_out, int variant,
+                                 const void *workspace, size_t workspace_bytes, void *stream);
+
 /* The pair-symmetric pass that also carries each body's potential, as
  * nbody_accel_potential does for the one-sided pass (the CAL IL loop of "CAL
  * programming (4)" keeps the same sum, m_j times its rsq result, in the w

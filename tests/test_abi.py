@@ -233,6 +233,36 @@ def test_symmetric_host_side(lib):
     assert f(vp(A), nb.NBODY_MAX_N, 1.0, 1e-4, vp(B), 0, vp(C), 1 << 62, None) == nb.NBODY_ERR_INVALID_ARG
 
 
+def test_symmetric_two_phase_host_side(lib):
+    """The two phases of the pair-symmetric pass check what each touches:
+    the tasks phase posmass, eps2 and the workspace, the reduce G, accel_out
+    and the workspace."""
+    count = nb.nbody_accel_symmetric_variant_count()
+    need = nb.nbody_accel_symmetric_workspace_bytes(1000, 0)
+    t = lib.nbody_accel_symmetric_tasks
+    assert t(vp(A), 0, 1e-4, 0, None, 0, None) == nb.NBODY_OK
+    assert t(vp(A), -1, 1e-4, 0, vp(C), need, None) == nb.NBODY_ERR_INVALID_ARG
+    assert t(vp(A), 1000, 1e-4, count, vp(C), need, None) == nb.NBODY_ERR_INVALID_ARG
+    assert t(vp(A), 1000, 0.0, 0, vp(C), need, None) == nb.NBODY_ERR_INVALID_ARG
+    assert t(vp(A), 1000, float("nan"), 0, vp(C), need, None) == nb.NBODY_ERR_INVALID_ARG
+    assert t(None, 1000, 1e-4, 0, vp(C), need, None) == nb.NBODY_ERR_INVALID_ARG
+    assert t(vp(A + 4), 1000, 1e-4, 0, vp(C), need, None) == nb.NBODY_ERR_ALIGNMENT
+    assert t(vp(A), 1000, 1e-4, 0, vp(C), need - 4, None) == nb.NBODY_ERR_WORKSPACE
+    assert t(vp(A), 1000, 1e-4, 0, vp(C + 4), need, None) == nb.NBODY_ERR_ALIGNMENT
+    assert t(vp(A), 1000, 1e-4, 0, vp(A - 64), need, None) == nb.NBODY_ERR_ALIAS
+    r = lib.nbody_accel_symmetric_reduce
+    assert r(0, 1.0, vp(B), 0, None, 0, None) == nb.NBODY_OK
+    assert r(1000, float("inf"), vp(B), 0, vp(C), need, None) == nb.NBODY_ERR_INVALID_ARG
+    assert r(1000, 1.0, vp(B), count, vp(C), need, None) == nb.NBODY_ERR_INVALID_ARG
+    assert r(1000, 1.0, None, 0, vp(C), need, None) == nb.NBODY_ERR_INVALID_ARG
+    assert r(1000, 1.0, vp(B + 8), 0, vp(C), need, None) == nb.NBODY_ERR_ALIGNMENT
+    assert r(1000, 1.0, vp(B), 0, None, need, None) == nb.NBODY_ERR_WORKSPACE
+    assert r(1000, 1.0, vp(B), 0, vp(C), need - 4, None) == nb.NBODY_ERR_WORKSPACE
+    assert r(1000, 1.0, vp(B), 0, vp(B - 64), need, None) == nb.NBODY_ERR_ALIAS
+    # the library's choice of variant for n when passed -1
+    assert t(vp(A), 1000, 0.0, -1, vp(C), 1 << 40, None) == nb.NBODY_ERR_INVALID_ARG
+
+
 def test_symmetric_potential_host_side(lib):
     count = nb.nbody_accel_symmetric_potential_variant_count()
     assert count >= 1

@@ -352,6 +352,24 @@ def test_symmetric_plummer1m_sampled():
     assert_parity(a, gpu_accel(pm, w.G, w.eps2).astype(np.float64), "symmetric vs one-sided 1m")
 
 
+@pytest.mark.parametrize("n,variant", [(5000, -1), (5000, 14), (70001, -1), (3001, 19)])
+def test_symmetric_two_phases_equal_one_call(n, variant):
+    """nbody_accel_symmetric_tasks then nbody_accel_symmetric_reduce give the
+    one-call result bitwise, and the tasks phase leaves accel_out alone."""
+    pm, _ = workloads.uniform_cube(n, seed=400 + n, masses="lognormal")
+    one = sym_accel(pm, 0.75, 1e-4, variant)
+    t = torch.from_numpy(pm).to(DEV)
+    out = torch.full_like(t, 7.0)
+    ws = torch.empty(nb.nbody_accel_symmetric_workspace_bytes(n, variant), dtype=torch.uint8,
+                     device=DEV)
+    nb.nbody_accel_symmetric_tasks(t, 1e-4, ws, variant)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+    nb.nbody_accel_symmetric_reduce(n, 0.75, out, ws, variant)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), one)
+
+
 @pytest.mark.parametrize("n", [40000, 131072, 262144])
 def test_symmetric_default_variant_at_switch_sizes(n):
     """The library's choice around its switches (2-, 4- and 8-body i-groups at
