@@ -391,3 +391,42 @@ def test_circular_binary_one_orbit():
         f"return error {np.abs(x - pm0[:, :3]).max():.2e}")
     assert worst <= (omega * dt) ** 2 + 1e-5
     assert np.abs(x - pm0[:, :3]).max() <= 2e-3
+
+
+# ---------------------------------------------------------------------------
+# Streams
+# ---------------------------------------------------------------------------
+
+def test_calls_on_side_streams_run_concurrently_and_match():
+    """Every entry point takes the stream it is queued on: the pair-symmetric
+    pass (one call and its two phases), the one-sided pass and the energy,
+    queued on two side streams with their own outputs and workspaces, match
+    the same calls made one after the other on the current stream bitwise."""
+    n = 20000
+    pm_np, vel_np = workloads.plummer(n, seed=77)
+    pm, vel = to_dev(pm_np), to_dev(vel_np)
+    ws_a = torch.empty(nb.nbody_accel_symmetric_workspace_bytes(n), dtype=torch.uint8, device=DEV)
+    ws_b = torch.empty_like(ws_a)
+    ews = torch.empty(nb.nbody_energy_workspace_bytes(n), dtype=torch.uint8, device=DEV)
+    ref_sym, ref_one = torch.empty_like(pm), torch.empty_like(pm)
+    ref_stats = torch.zeros(8, dtype=torch.float64, device=DEV)
+    nb.nbody_accel_symmetric(pm, 1.0, 1e-4, ref_sym, ws_a)
+    nb.nbody_accel(pm, 1.0, 1e-4, ref_one)
+    nb.nbody_energy(pm, vel, 1.0, 1e-4, ews, ref_stats)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()   # default priority
+    out_sym, out_two, out_one = (torch.full_like(pm, float("nan")) for _ in range(3))
+    stats = torch.zeros(8, dtype=torch.float64, device=DEV)
+    ews2 = torch.empty_like(ews)
+    torch.cuda.synchronize()
+    nb.nbody_accel_symmetric(pm, 1.0, 1e-4, out_sym, ws_a, stream=s1)
+    nb.nbody_accel_symmetric_tasks(pm, 1e-4, ws_b, stream=s2)
+    nb.nbody_accel(pm, 1.0, 1e-4, out_one, stream=s1)
+    nb.nbody_accel_symmetric_reduce(n, 1.0, out_two, ws_b, stream=s2)
+    nb.nbody_energy(pm, vel, 1.0, 1e-4, ews2, stats, stream=s2)
+    s1.synchronize()
+    s2.synchronize()
+    assert torch.equal(out_sym, ref_sym)
+    assert torch.equal(out_two, ref_sym)
+    assert torch.equal(out_one, ref_one)
+    assert torch.equal(stats, ref_stats)
