@@ -86,7 +86,13 @@ int nbody_abi_version(void);
  *   posmass    [n] float4 (x, y, z, m), read only.
  *   G          gravitational constant (finite).
  *   eps2       squared softening length eps^2 (> 0, finite).  The README's
- *              constants table calls this EPS2 (section 6.1).
+ *              constants table calls this EPS2 (section 6.1).  The pair
+ *              terms are fp32: m_j * eps2^(-3/2) must stay below the fp32
+ *              maximum (3.4e38) for every body, i.e. eps2 above about
+ *              (m_max / 3.4e38)^(2/3) (2e-26 for m = 1, 2e-30 for m = 1e-6).
+ *              Below it the self term m_i eps^-3 * 0 is inf * 0 and every
+ *              acceleration comes out NaN; this is not checked (the masses
+ *              are device data).  The same holds for every force pass.
  *   accel_out  [n] float4, written: (ax, ay, az, 0).  Must not overlap
  *              posmass (NBODY_ERR_ALIAS).
  * The library picks a variant from n (nbody_accel_variant_for_n). */

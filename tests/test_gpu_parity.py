@@ -528,6 +528,21 @@ def test_one_massive_body_among_test_particles(path):
 
 
 @pytest.mark.parametrize("path", sorted(PATHS))
+def test_tiny_softening_fp32_range(path):
+    """The documented fp32 limit of eps2: with unit masses, eps2 = 1e-24 keeps
+    m eps^-3 = 1e36 finite and the result matches the oracle (the self term
+    is exactly 0); eps2 = 1e-27 overflows it and every row is NaN."""
+    n = 3000
+    pm, _ = workloads.uniform_cube(n, seed=63)
+    pm[:, 3] = 1.0
+    a = PATHS[path](pm, 1.0, 1e-24)
+    assert np.all(np.isfinite(a))
+    rows = sample_rows(n, 128, seed=10)
+    assert_parity(a[rows], ref_accel(pm, 1.0, 1e-24, rows), f"eps2 1e-24 {path}")
+    assert np.all(np.isnan(PATHS[path](pm, 1.0, 1e-27)[:, :3]))
+
+
+@pytest.mark.parametrize("path", sorted(PATHS))
 @pytest.mark.parametrize("bad", ["nan_x", "nan_mass"])
 def test_nan_body_propagates(path, bad):
     """The hot path does not check its data: a body with a NaN coordinate or a
