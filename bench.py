@@ -78,10 +78,18 @@ def cpu_baseline(pm_np, acc0_np, w, seconds):
     l2 = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
     per = float((np.linalg.norm(got - ref, axis=1) / np.linalg.norm(ref, axis=1)).max())
     inter = rows * w.n
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")),
+                         None)
+    except OSError:
+        pass
     return {
         "value": inter / dt / 1e9,
         "unit": "billion interactions/s",
         "cores": oracle.num_threads(),
+        "cpu_model": model,
         "kind": "oracle",
         "sample": f"{rows} of {w.n} bodies, each summed over all {w.n} (float64, "
                   f"{inter:.3e} interactions in {dt:.1f} s)",
