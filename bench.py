@@ -2,19 +2,23 @@
 """Throughput of direct all-pairs softened gravity on one MI355X.
 
 One step = one kick-drift-kick leapfrog step of the whole body set:
-nbody_leapfrog_step (kick + drift), nbody_accel (the O(N^2) force pass) and
-nbody_kick (closing half-kick).  The default workload is the N = 1,048,576
-Plummer sphere (equal masses 1/N, eps^2 = 1e-4, dt = 1e-4).  value = N^2
-body-body interactions per step / seconds per step, in billions per second.
+nbody_leapfrog_step (kick + drift), the O(N^2) force pass and nbody_kick
+(closing half-kick).  The force pass is the pair-symmetric one
+(nbody_accel_symmetric, launched as its two phases: the panel-pair kernel,
+then the reduce) unless --path tile selects the one-sided nbody_accel.  The
+default workload is the N = 1,048,576 Plummer sphere (equal masses 1/N,
+eps^2 = 1e-4, dt = 1e-4).  value = N^2 body-body interactions per step /
+seconds per step, in billions per second.
 
 Inputs are resident in HBM before the timed region; the region is bracketed by
-torch.cuda.synchronize() on both sides.  The force pass's dominant kernel (the
-panel-pair kernel of the pair-symmetric pass, launched through
-nbody_accel_symmetric_tasks, or the one-sided kernel) is timed with HIP events
-recorded on the stream it is launched on (the current torch stream) around
-every launch; the roofline object reports it against the MI355X FP32 vector
-peak at 20 flops per interaction (the count of "Cuda Nbody Notes").  force_ms
-is the whole pass, the pair-symmetric reduce kernel included.
+torch.cuda.synchronize() on both sides.  Every GPU time is taken with the
+library's own HIP events (nbody_timer_*, nbody_time_accel), recorded on the
+stream the kernels are launched on (the current torch stream); torch only
+provides device memory and the stream.  The roofline object reports the
+force pass's dominant kernel (the panel-pair kernel, or the one-sided kernel)
+against the MI355X FP32 vector peak at 20 flops per interaction (the count of
+"Cuda Nbody Notes"); force_ms is the whole pass, the pair-symmetric reduce
+kernel included, and force_pass_frac the same ratio for the whole pass.
 
 The energy / momentum pass (a checkpoint diagnostic, not part of a step) is
 timed separately.  The CPU baseline is the double-precision oracle timed on a
@@ -104,17 +108,18 @@ SPLITJ_TREES = ((32, 1), (32, 2), (32, 4), (64, 1), (64, 2), (128, 2), (256, 4))
 SPLITJ_MAX_WORKSPACE = 16 << 30
 
 
-def _time(torch, fn, reps):
-    stream = torch.cuda.current_stream()
+def _time(nb, fn, reps):
+    """Milliseconds of each of `reps` calls of fn (after one untimed call),
+    between marks of the library's timer on the current stream."""
     fn()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(reps)]
-    for a, b in ev:
-        a.record(stream)
+    t = nb.Timer(2 * reps)
+    for r in range(reps):
+        t.mark(2 * r)
         fn()
-        b.record(stream)
-    torch.cuda.synchronize()
-    return [a.elapsed_time(b) for a, b in ev]
+        t.mark(2 * r + 1)
+    ms = [t.elapsed_ms(2 * r, 2 * r + 1) for r in range(reps)]
+    t.close()
+    return ms
 
 
 def _sweep_line(w, ms, **kw):
@@ -132,14 +137,14 @@ def sweep(nb, torch, w, pm, acc, reps, paths):
     two-pass split-j decomposition for a range of chunk widths (workspace
     permitting)."""
     for v in range(nb.nbody_accel_variant_count() if "tile" in paths else 0):
-        ms = _time(torch, lambda: nb.nbody_accel_variant(pm, w.G, w.eps2, acc, v), reps)
+        ms = _time(nb, lambda: nb.nbody_accel_variant(pm, w.G, w.eps2, acc, v), reps)
         _sweep_line(w, ms, variant=v, tiling=nb.nbody_accel_variant_info(v))
     for v in range(nb.nbody_accel_symmetric_variant_count() if "symmetric" in paths else 0):
         need = nb.nbody_accel_symmetric_workspace_bytes(w.n, v)
         if need > 4 * SPLITJ_MAX_WORKSPACE:
             continue
         ws = torch.empty(need, dtype=torch.uint8, device=pm.device)
-        ms = _time(torch, lambda: nb.nbody_accel_symmetric(pm, w.G, w.eps2, acc, ws, v), reps)
+        ms = _time(nb, lambda: nb.nbody_accel_symmetric(pm, w.G, w.eps2, acc, ws, v), reps)
         _sweep_line(w, ms, symmetric_variant=v, panel=nb.nbody_accel_symmetric_panel(v),
                     workspace_bytes=need)
         del ws
@@ -148,7 +153,7 @@ def sweep(nb, torch, w, pm, acc, reps, paths):
         ni = w.n // 8
         out = torch.empty((ni, 4), dtype=torch.float32, device=pm.device)
         for v in range(nb.nbody_accel_variant_count()):
-            ms = _time(torch, lambda: nb.nbody_accel_range(pm, 0, ni, w.G, w.eps2, out, v), reps)
+            ms = _time(nb, lambda: nb.nbody_accel_range(pm, 0, ni, w.G, w.eps2, out, v), reps)
             best = min(ms)
             inter = float(ni) * float(w.n)
             tflops = FLOPS_PER_INTERACTION * inter / (best * 1e-3) / 1e12
@@ -161,7 +166,7 @@ def sweep(nb, torch, w, pm, acc, reps, paths):
         if need > SPLITJ_MAX_WORKSPACE or -(-w.n // j_chunk) > 65535:
             continue
         ws = torch.empty(need, dtype=torch.uint8, device=pm.device)
-        ms = _time(torch, lambda: nb.nbody_accel_splitj(pm, w.G, w.eps2, acc, j_chunk, ws), reps)
+        ms = _time(nb, lambda: nb.nbody_accel_splitj(pm, w.G, w.eps2, acc, j_chunk, ws), reps)
         _sweep_line(w, ms, splitj_chunk=j_chunk, workspace_bytes=need)
         del ws
     for j_chunk, terms in SPLITJ_TREES if "splitj" in paths else ():
@@ -169,7 +174,7 @@ def sweep(nb, torch, w, pm, acc, reps, paths):
         if need > SPLITJ_MAX_WORKSPACE or -(-w.n // j_chunk) > 65535:
             continue
         ws = torch.empty(need, dtype=torch.uint8, device=pm.device)
-        ms = _time(torch, lambda: nb.nbody_accel_splitj_tree(pm, w.G, w.eps2, acc, j_chunk, terms,
+        ms = _time(nb, lambda: nb.nbody_accel_splitj_tree(pm, w.G, w.eps2, acc, j_chunk, terms,
                                                              ws), reps)
         _sweep_line(w, ms, splitj_tree_chunk=j_chunk, terms=terms, workspace_bytes=need)
         del ws
@@ -208,19 +213,19 @@ def suite(nb, torch, names):
         force = {}
         tv = nb.nbody_accel_variant_for_n(w.n)
         force[f"one_sided_v{tv}"] = _stats(
-            w, _time(torch, lambda: nb.nbody_accel_variant(pm, w.G, w.eps2, acc, tv), reps))
+            w, _time(nb, lambda: nb.nbody_accel_variant(pm, w.G, w.eps2, acc, tv), reps))
         sv = nb.nbody_accel_symmetric_variant_for_n(w.n)
         sym_ws = torch.empty(max(nb.nbody_accel_symmetric_workspace_bytes(w.n, sv), 16),
                              dtype=torch.uint8, device=dev)
         force[f"symmetric_v{sv}"] = _stats(
-            w, _time(torch, lambda: nb.nbody_accel_symmetric(pm, w.G, w.eps2, acc, sym_ws, sv),
+            w, _time(nb, lambda: nb.nbody_accel_symmetric(pm, w.G, w.eps2, acc, sym_ws, sv),
                      reps))
         if w.n >= 100000:
             pv = nb.nbody_accel_symmetric_potential_variant_for_n(w.n)
             pot_ws = torch.empty(nb.nbody_accel_symmetric_potential_workspace_bytes(w.n, pv),
                                  dtype=torch.uint8, device=dev)
             force[f"symmetric_potential_v{pv}"] = _stats(
-                w, _time(torch, lambda: nb.nbody_accel_symmetric_potential(
+                w, _time(nb, lambda: nb.nbody_accel_symmetric_potential(
                     pm, w.G, w.eps2, acc, pot_ws, pv), reps))
             del pot_ws
         if name == "plummer1m":
@@ -229,26 +234,26 @@ def suite(nb, torch, names):
             mass = pm[:, 3].contiguous()
             acc3 = torch.empty_like(pos3)
             force[f"one_sided_v{tv}_float3_aos"] = _stats(
-                w, _time(torch, lambda: nb.nbody_accel_f3aos(pos3, mass, w.G, w.eps2, acc3),
+                w, _time(nb, lambda: nb.nbody_accel_f3aos(pos3, mass, w.G, w.eps2, acc3),
                          reps))
             xyz = [pm[:, k].contiguous() for k in range(4)]
             axyz = [torch.empty_like(xyz[0]) for _ in range(3)]
             force[f"one_sided_v{tv}_soa"] = _stats(
-                w, _time(torch, lambda: nb.nbody_accel_soa(*xyz, w.G, w.eps2, *axyz), reps))
+                w, _time(nb, lambda: nb.nbody_accel_soa(*xyz, w.G, w.eps2, *axyz), reps))
             del pos3, mass, acc3, xyz, axyz
         if name == "lognormal128k":
             for j_chunk in SPLITJ_CHUNKS:
                 ws = torch.empty(nb.nbody_accel_splitj_workspace_bytes(w.n, j_chunk),
                                  dtype=torch.uint8, device=dev)
                 force[f"splitj_J{j_chunk}"] = _stats(
-                    w, _time(torch, lambda: nb.nbody_accel_splitj(pm, w.G, w.eps2, acc, j_chunk,
+                    w, _time(nb, lambda: nb.nbody_accel_splitj(pm, w.G, w.eps2, acc, j_chunk,
                                                                   ws), reps))
                 del ws
             for j_chunk, terms in SPLITJ_TREES:
                 ws = torch.empty(nb.nbody_accel_splitj_tree_workspace_bytes(w.n, j_chunk, terms),
                                  dtype=torch.uint8, device=dev)
                 force[f"splitj_tree_J{j_chunk}_F{terms}"] = _stats(
-                    w, _time(torch, lambda: nb.nbody_accel_splitj_tree(pm, w.G, w.eps2, acc,
+                    w, _time(nb, lambda: nb.nbody_accel_splitj_tree(pm, w.G, w.eps2, acc,
                                                                        j_chunk, terms, ws), reps))
                 del ws
         out["force"] = force
@@ -267,19 +272,19 @@ def suite(nb, torch, names):
             vel = torch.from_numpy(vel_np).to(dev)
             e0 = nb.energy(pm, vel, w.G, w.eps2)
             fpass()
-            stream = torch.cuda.current_stream()
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(w.steps + 1)]
+            timer = nb.Timer(w.steps + 1)
             torch.cuda.synchronize()
             t0 = time.perf_counter()
-            ev[0].record(stream)
+            timer.mark(0)
             for k in range(w.steps):
                 nb.nbody_leapfrog_step(pm, vel, acc, w.dt)
                 fpass()
                 nb.nbody_kick(vel, acc, 0.5 * w.dt)
-                ev[k + 1].record(stream)
+                timer.mark(k + 1)
             torch.cuda.synchronize()
             wall = time.perf_counter() - t0
-            step_ms = [ev[k].elapsed_time(ev[k + 1]) for k in range(w.steps)]
+            step_ms = [timer.elapsed_ms(k, k + 1) for k in range(w.steps)]
+            timer.close()
             e1 = nb.energy(pm, vel, w.G, w.eps2)
             dp = sum((e1[c] - e0[c]) ** 2 for c in ("Px", "Py", "Pz")) ** 0.5
             out["run"] = {"steps": w.steps, "dt": w.dt, "force_pass": best,
@@ -297,7 +302,7 @@ def suite(nb, torch, names):
                 nb.nbody_accel_symmetric(pm, w.G, w.eps2, acc, sv_ws, sv)
                 nb.nbody_kick(vel, acc, 0.5 * w.dt)
             nb.nbody_accel_symmetric(pm, w.G, w.eps2, acc, sym_ws, sv)
-            out["kdk_step"] = _stats(w, _time(torch, kdk, 3))
+            out["kdk_step"] = _stats(w, _time(nb, kdk, 3))
             del vel
         print(json.dumps(out), flush=True)
         del pm, acc, sym_ws
@@ -338,6 +343,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target length of the oracle CPU-baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-one-sided", action="store_true",
+                    help="skip timing the one-sided pass beside the pair-symmetric one")
     ap.add_argument("--sweep", action="store_true",
                     help="time the force pass of every compiled variant (one JSON line each) "
                          "instead of the step benchmark")
@@ -429,41 +436,50 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    stream = torch.cuda.current_stream()
-    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
-          for _ in range(args.steps)]
+    # marks: 0 at the start, then per step k: after the kick-drift (4k + 1),
+    # after the dominant kernel (4k + 2), after the force pass (4k + 3) and
+    # after the closing half-kick (4k + 4)
+    timer = nb.Timer(4 * args.steps + 1)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    timer.mark(0)
     for k in range(args.steps):
         nb.nbody_leapfrog_step(pm, vel, acc, dt)
-        ev[k][0].record(stream)
+        timer.mark(4 * k + 1)
         force_main()
-        ev[k][1].record(stream)
+        timer.mark(4 * k + 2)
         force_rest()
-        ev[k][2].record(stream)
+        timer.mark(4 * k + 3)
         nb.nbody_kick(vel, acc, 0.5 * dt)
+        timer.mark(4 * k + 4)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    kernel_ms = [a.elapsed_time(b) for a, b, _ in ev]    # the dominant kernel
-    force_ms = [a.elapsed_time(c) for a, _, c in ev]     # the whole force pass
+    kernel_ms = [timer.elapsed_ms(4 * k + 1, 4 * k + 2) for k in range(args.steps)]
+    force_ms = [timer.elapsed_ms(4 * k + 1, 4 * k + 3) for k in range(args.steps)]
+    step_ms = [timer.elapsed_ms(4 * k, 4 * k + 4) for k in range(args.steps)]
+    timer.close()
     kernel_avg = sum(kernel_ms) / len(kernel_ms)
     force_avg = sum(force_ms) / len(force_ms)
     inter = float(w.n) * float(w.n)
     value = inter / (ms_per_step * 1e-3) / 1e9
     achieved = FLOPS_PER_INTERACTION * inter / (kernel_avg * 1e-3) / 1e12
-    log(f"step {ms_per_step:.3f} ms, force pass {force_avg:.3f} ms, its main kernel "
-        f"{kernel_avg:.3f} ms (min {min(kernel_ms):.3f}), {value:.1f} G interactions/s per step")
+    pass_tflops = FLOPS_PER_INTERACTION * inter / (force_avg * 1e-3) / 1e12
+    log(f"step {ms_per_step:.3f} ms (events {sum(step_ms) / len(step_ms):.3f}), force pass "
+        f"{force_avg:.3f} ms, its main kernel {kernel_avg:.3f} ms (min {min(kernel_ms):.3f}), "
+        f"{value:.1f} G interactions/s per step")
+
+    # the one-sided pass (nbody_accel, no workspace) on the same positions, for
+    # comparison
+    one_ms = None
+    if args.path == "symmetric" and not args.no_one_sided:
+        one_ms, _ = nb.nbody_time_accel(pm, w.G, w.eps2, acc, nb.NBODY_PASS_ONE_SIDED, 2)
+        log(f"one-sided nbody_accel: {min(one_ms):.3f} ms")
 
     # energy diagnostic (outside the timed steps)
     ws = torch.empty(nb.nbody_energy_workspace_bytes(w.n), dtype=torch.uint8, device=dev)
     stats = torch.zeros(8, dtype=torch.float64, device=dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    nb.nbody_energy(pm, vel, w.G, w.eps2, ws, stats)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    energy_ms = e0.elapsed_time(e1)
+    energy_ms = _time(nb, lambda: nb.nbody_energy(pm, vel, w.G, w.eps2, ws, stats), 1)[0]
     checkpoint_ms = None
     if args.path == "symmetric":
         # a checkpoint step's force pass with the potentials in accel.w, then
@@ -474,15 +490,18 @@ def main():
         pws = torch.empty(nb.nbody_energy_from_potential_workspace_bytes(w.n),
                           dtype=torch.uint8, device=dev)
         acc_pot = torch.empty_like(acc)
-        nb.nbody_accel_symmetric_potential(pm, w.G, w.eps2, acc_pot, pot_ws, pv)
-        e0.record(stream)
-        nb.nbody_accel_symmetric_potential(pm, w.G, w.eps2, acc_pot, pot_ws, pv)
-        nb.nbody_energy_from_potential(pm, vel, acc_pot, pws, stats)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        checkpoint_ms = e0.elapsed_time(e1)
+
+        def checkpoint():
+            nb.nbody_accel_symmetric_potential(pm, w.G, w.eps2, acc_pot, pot_ws, pv)
+            nb.nbody_energy_from_potential(pm, vel, acc_pot, pws, stats)
+        checkpoint_ms = _time(nb, checkpoint, 1)[0]
         del pot_ws, pws, acc_pot
 
+    # FP32 arithmetic the pair step actually issues (rsq not counted), per
+    # counted interaction: the pair-symmetric step evaluates each pair once
+    # for two interactions (3 sub, 1 fma, 2 fmac, 4 mul, 6 fmac = 25 flops),
+    # the one-sided step 3 sub, 3 fma, 3 mul, 3 fmac = 18 flops
+    issued = 12.5 if args.path == "symmetric" else 18.0
     traffic = traffic_per_launch(args.path, variant, w.name)
     out = {
         "metric": METRIC,
@@ -511,6 +530,13 @@ def main():
         "pct_fp32_peak": 100.0 * achieved / PEAK_FP32_TFLOPS,
         "force_ms": force_avg,
         "force_kernel_ms": kernel_avg,
+        "force_pass_frac": pass_tflops / PEAK_FP32_TFLOPS,
+        "pairs_evaluated_per_interaction": 0.5 if args.path == "symmetric" else 1.0,
+        "fp32_flops_issued_per_interaction": issued,
+        "fp32_issued_frac": issued * inter / (kernel_avg * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
+        "one_sided_force_ms": min(one_ms) if one_ms else None,
+        "one_sided_frac": (FLOPS_PER_INTERACTION * inter / (min(one_ms) * 1e-3) / 1e12
+                           / PEAK_FP32_TFLOPS) if one_ms else None,
         "energy_ms": energy_ms,
         "checkpoint_force_energy_ms": checkpoint_ms,
         "roofline": {

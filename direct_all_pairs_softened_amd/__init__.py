@@ -47,7 +47,14 @@ EXPORTS = (
     "nbody_accel_f3aos", "nbody_accel_soa",
     "nbody_leapfrog_step", "nbody_kick",
     "nbody_energy", "nbody_energy_workspace_bytes",
+    "nbody_timer_create", "nbody_timer_mark", "nbody_timer_elapsed_ms", "nbody_timer_destroy",
+    "nbody_time_accel",
 )
+
+# Force passes of nbody_time_accel.
+NBODY_PASS_ONE_SIDED = 0
+NBODY_PASS_SYMMETRIC = 1
+NBODY_PASS_SYMMETRIC_POTENTIAL = 2
 
 ENERGY_FIELDS = ("K", "W", "E", "Px", "Py", "Pz", "M")
 
@@ -81,7 +88,7 @@ def load_library(path: str | None = None):
         "nbody_accel": (c_int, [vp, c_i64, c_f, c_f, vp, vp]),
         "nbody_accel_variant": (c_int, [vp, c_i64, c_f, c_f, vp, c_int, vp]),
         "nbody_accel_variant_count": (c_int, []),
-        "nbody_accel_variant_info": (c_int, [c_int, pint, pint, pint, pint, pint]),
+        "nbody_accel_variant_info": (c_int, [c_int, pint, pint, pint, pint, pint, pint]),
         "nbody_accel_variant_for_n": (c_int, [c_i64]),
         "nbody_accel_potential": (c_int, [vp, c_i64, c_f, c_f, vp, vp]),
         "nbody_energy_from_potential": (c_int, [vp, vp, vp, c_i64, vp, c_sz, vp, vp]),
@@ -111,6 +118,12 @@ def load_library(path: str | None = None):
         "nbody_kick": (c_int, [vp, vp, c_f, c_i64, vp]),
         "nbody_energy": (c_int, [vp, vp, c_i64, c_f, c_f, vp, c_sz, vp, vp]),
         "nbody_energy_workspace_bytes": (c_sz, [c_i64]),
+        "nbody_timer_create": (c_int, [c_int, ctypes.POINTER(vp)]),
+        "nbody_timer_mark": (c_int, [vp, c_int, vp]),
+        "nbody_timer_elapsed_ms": (c_int, [vp, c_int, c_int, ctypes.POINTER(c_f)]),
+        "nbody_timer_destroy": (c_int, [vp]),
+        "nbody_time_accel": (c_int, [vp, c_i64, c_f, c_f, vp, c_int, c_int, vp, c_sz, c_int,
+                                     ctypes.POINTER(c_f), ctypes.POINTER(c_f), vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -200,10 +213,10 @@ def nbody_accel_variant_count() -> int:
 
 
 def nbody_accel_variant_info(v: int) -> dict:
-    vals = [ctypes.c_int() for _ in range(5)]
+    vals = [ctypes.c_int() for _ in range(6)]
     _check(load_library().nbody_accel_variant_info(int(v), *[ctypes.byref(x) for x in vals]),
            "nbody_accel_variant_info")
-    keys = ("bodies_per_lane", "tile", "waves_per_block", "split", "staging")
+    keys = ("bodies_per_lane", "tile", "waves_per_block", "split", "staging", "unroll")
     return {k: x.value for k, x in zip(keys, vals)}
 
 
@@ -443,6 +456,61 @@ def nbody_energy(posmass, vel, G: float, eps2: float, workspace, stats_out, stre
            "nbody_energy")
 
 
+class Timer:
+    """nbody_timer: ``marks`` HIP events owned by the library, recorded on the
+    stream the timed work runs on (``mark``), read back with ``elapsed_ms``
+    (which waits for the later event)."""
+
+    def __init__(self, marks: int):
+        self._t = ctypes.c_void_p()
+        _check(load_library().nbody_timer_create(int(marks), ctypes.byref(self._t)),
+               "nbody_timer_create")
+        self.marks = int(marks)
+
+    def mark(self, i: int, stream=None):
+        _check(load_library().nbody_timer_mark(self._t, int(i), _stream(stream)),
+               "nbody_timer_mark")
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        _check(load_library().nbody_timer_elapsed_ms(self._t, int(a), int(b), ctypes.byref(ms)),
+               "nbody_timer_elapsed_ms")
+        return float(ms.value)
+
+    def close(self):
+        if self._t:
+            load_library().nbody_timer_destroy(self._t)
+            self._t = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def nbody_time_accel(posmass, G: float, eps2: float, accel_out, pass_kind: int, reps: int,
+                     variant: int = -1, workspace=None, stream=None):
+    """Runs ``reps`` force passes timed with the library's HIP events (waits
+    for them).  Returns (pass_ms, kernel_ms), two lists of ``reps`` floats."""
+    n = _n_of(posmass)
+    if _n_of(accel_out) != n:
+        raise ValueError("accel_out must have N rows")
+    if workspace is None:
+        ws, nbytes = ctypes.c_void_p(), 0
+    else:
+        ws = _dev(workspace, "workspace")
+        nbytes = workspace.numel() * workspace.element_size()
+    pass_ms = (ctypes.c_float * max(int(reps), 1))()
+    kernel_ms = (ctypes.c_float * max(int(reps), 1))()
+    _check(load_library().nbody_time_accel(_f32(posmass, "posmass", (4,)), n, G, eps2,
+                                           _f32(accel_out, "accel_out", (4,)), int(pass_kind),
+                                           int(variant), ws, nbytes, int(reps), pass_ms,
+                                           kernel_ms, _stream(stream)),
+           "nbody_time_accel")
+    return list(pass_ms)[:reps], list(kernel_ms)[:reps]
+
+
 # ---------------------------------------------------------------------------
 # conveniences built only from the entry points above
 # ---------------------------------------------------------------------------
@@ -469,9 +537,30 @@ def energy(posmass, vel, G: float = 1.0, eps2: float = 1e-4) -> dict:
     return dict(zip(ENERGY_FIELDS, vals[:7]))
 
 
-def kdk_step(posmass, vel, accel_buf, G: float, eps2: float, dt: float, stream=None):
-    """One kick-drift-kick step.  accel_buf must hold a(x) on entry and holds
-    a(x_new) on return."""
+class SymmetricPass:
+    """nbody_accel_symmetric with its workspace allocated once, for n bodies:
+    ``SymmetricPass(n, device)(posmass, G, eps2, accel_out)``."""
+
+    def __init__(self, n: int, device, variant: int = -1):
+        self.n = int(n)
+        self.variant = int(variant)
+        self.workspace = _torch().empty(
+            max(nbody_accel_symmetric_workspace_bytes(self.n, self.variant), 16),
+            dtype=_torch().uint8, device=device)
+
+    def __call__(self, posmass, G: float, eps2: float, accel_out, stream=None):
+        nbody_accel_symmetric(posmass, G, eps2, accel_out, self.workspace, self.variant, stream)
+
+
+def kdk_step(posmass, vel, accel_buf, G: float, eps2: float, dt: float, stream=None,
+             force=None):
+    """One kick-drift-kick step: nbody_leapfrog_step, the force pass at the new
+    positions, nbody_kick with dt/2.  accel_buf must hold a(x) on entry and
+    holds a(x_new) on return.  force: None for nbody_accel, or a callable
+    force(posmass, G, eps2, accel_out, stream) such as a SymmetricPass."""
     nbody_leapfrog_step(posmass, vel, accel_buf, dt, stream)
-    nbody_accel(posmass, G, eps2, accel_buf, stream)
+    if force is None:
+        nbody_accel(posmass, G, eps2, accel_buf, stream)
+    else:
+        force(posmass, G, eps2, accel_buf, stream)
     nbody_kick(vel, accel_buf, 0.5 * dt, stream)

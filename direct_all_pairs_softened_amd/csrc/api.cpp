@@ -7,6 +7,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "nbody_internal.hpp"
 
 namespace {
@@ -33,8 +35,10 @@ int hip_status(hipError_t e) { return e == hipSuccess ? NBODY_OK : NBODY_ERR_HIP
 
 hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
-int force_aos4(const float *posmass, int64_t n, float G, float eps2, float *accel_out,
-               int variant, void *stream) {
+// The checks of the one-sided float4 pass; NBODY_OK with n == 0 means there
+// is nothing to launch.
+int force_aos4_check(const float *posmass, int64_t n, float G, float eps2,
+                     const float *accel_out, int variant) {
   if (!n_ok(n)) return NBODY_ERR_INVALID_ARG;
   if (int s = check_consts(G, eps2)) return s;
   if (!nbody::force_variant(variant)) return NBODY_ERR_INVALID_ARG;
@@ -43,6 +47,13 @@ int force_aos4(const float *posmass, int64_t n, float G, float eps2, float *acce
   if (!aligned(posmass, 16) || !aligned(accel_out, 16)) return NBODY_ERR_ALIGNMENT;
   const size_t bytes = (size_t)n * 16;
   if (overlap(posmass, bytes, accel_out, bytes)) return NBODY_ERR_ALIAS;
+  return NBODY_OK;
+}
+
+int force_aos4(const float *posmass, int64_t n, float G, float eps2, float *accel_out,
+               int variant, void *stream) {
+  if (int s = force_aos4_check(posmass, n, G, eps2, accel_out, variant)) return s;
+  if (n == 0) return NBODY_OK;
   BodyArrays b;
   b.posmass = posmass;
   b.accel4 = accel_out;
@@ -79,7 +90,7 @@ int nbody_abi_version(void) { return NBODY_ABI_VERSION; }
 int nbody_accel_variant_count(void) { return nbody::force_variant_count(); }
 
 int nbody_accel_variant_info(int v, int *bodies_per_lane, int *tile, int *waves_per_block,
-                             int *split, int *staging) {
+                             int *split, int *staging, int *unroll) {
   const nbody::ForceVariant *fv = nbody::force_variant(v);
   if (!fv) return NBODY_ERR_INVALID_ARG;
   if (bodies_per_lane) *bodies_per_lane = fv->bodies_per_lane;
@@ -87,6 +98,7 @@ int nbody_accel_variant_info(int v, int *bodies_per_lane, int *tile, int *waves_
   if (waves_per_block) *waves_per_block = fv->waves;
   if (split) *split = fv->split;
   if (staging) *staging = fv->staging;
+  if (unroll) *unroll = fv->unroll;
   return NBODY_OK;
 }
 
@@ -430,6 +442,131 @@ int nbody_energy(const float *posmass, const float *vel, int64_t n, float G, flo
     return NBODY_ERR_ALIAS;
   return hip_status(nbody::launch_energy(posmass, vel, (int)n, G, eps2, workspace, stats_out,
                                          as_stream(stream)));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Timing: HIP events recorded on the caller's stream around the timed work.
+// ---------------------------------------------------------------------------
+
+struct nbody_timer {
+  std::vector<hipEvent_t> ev;
+};
+
+namespace {
+
+constexpr int kMaxTimerMarks = 1 << 20;
+constexpr int kMaxTimedReps = 1 << 16;
+
+// NBODY_OK when `stream` is not being captured into a graph.
+int not_capturing(hipStream_t stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return NBODY_ERR_HIP;
+  return cs == hipStreamCaptureStatusNone ? NBODY_OK : NBODY_ERR_INVALID_ARG;
+}
+
+void destroy_events(std::vector<hipEvent_t> &ev) {
+  for (hipEvent_t &e : ev)
+    if (e) (void)hipEventDestroy(e);
+  ev.clear();
+}
+
+hipError_t create_events(std::vector<hipEvent_t> &ev, int count) {
+  ev.assign(count, nullptr);
+  for (hipEvent_t &e : ev) {
+    const hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      e = nullptr;
+      destroy_events(ev);
+      return r;
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nbody_timer_create(int marks, nbody_timer **timer_out) {
+  if (!timer_out || marks < 1 || marks > kMaxTimerMarks) return NBODY_ERR_INVALID_ARG;
+  *timer_out = nullptr;
+  nbody_timer *t = new nbody_timer;
+  if (create_events(t->ev, marks) != hipSuccess) {
+    delete t;
+    return NBODY_ERR_HIP;
+  }
+  *timer_out = t;
+  return NBODY_OK;
+}
+
+int nbody_timer_mark(nbody_timer *timer, int mark, void *stream) {
+  if (!timer || mark < 0 || mark >= (int)timer->ev.size()) return NBODY_ERR_INVALID_ARG;
+  if (int s = not_capturing(as_stream(stream))) return s;
+  return hip_status(hipEventRecord(timer->ev[mark], as_stream(stream)));
+}
+
+int nbody_timer_elapsed_ms(nbody_timer *timer, int from, int to, float *ms_out) {
+  const int m = timer ? (int)timer->ev.size() : 0;
+  if (!timer || !ms_out || from < 0 || from >= m || to < 0 || to >= m)
+    return NBODY_ERR_INVALID_ARG;
+  hipError_t e = hipEventSynchronize(timer->ev[to]);
+  if (e == hipSuccess) e = hipEventElapsedTime(ms_out, timer->ev[from], timer->ev[to]);
+  return hip_status(e);
+}
+
+int nbody_timer_destroy(nbody_timer *timer) {
+  if (!timer) return NBODY_OK;
+  destroy_events(timer->ev);
+  delete timer;
+  return NBODY_OK;
+}
+
+int nbody_time_accel(const float *posmass, int64_t n, float G, float eps2, float *accel_out,
+                     int pass, int variant, void *workspace, size_t workspace_bytes, int reps,
+                     float *pass_ms, float *kernel_ms, void *stream) {
+  if (n == 0 || reps < 1 || reps > kMaxTimedReps || !pass_ms) return NBODY_ERR_INVALID_ARG;
+  const bool one_sided = pass == NBODY_PASS_ONE_SIDED;
+  const bool pot = pass == NBODY_PASS_SYMMETRIC_POTENTIAL;
+  if (!one_sided && pass != NBODY_PASS_SYMMETRIC && !pot) return NBODY_ERR_INVALID_ARG;
+  int v;
+  if (one_sided) {
+    v = variant < 0 ? nbody::force_variant_for_n(n) : variant;
+    if (int s = force_aos4_check(posmass, n, G, eps2, accel_out, v)) return s;
+  } else {
+    v = sym_variant(variant, n, pot);
+    if (int s = sym_check(posmass, n, G, eps2, accel_out, v, pot, workspace, workspace_bytes,
+                          true, true))
+      return s;
+  }
+  const hipStream_t st = as_stream(stream);
+  if (int s = not_capturing(st)) return s;
+  // per pass: start, after the dominant kernel, end
+  std::vector<hipEvent_t> ev;
+  hipError_t e = create_events(ev, 3 * reps);
+  BodyArrays b;
+  b.posmass = posmass;
+  b.accel4 = accel_out;
+  for (int r = 0; r < reps && e == hipSuccess; ++r) {
+    e = hipEventRecord(ev[3 * r], st);
+    if (e == hipSuccess)
+      e = one_sided ? nbody::launch_force(v, Layout::Aos4, b, (int)n, 0, (int)n, G, eps2, st)
+                    : nbody::launch_symmetric_tasks(posmass, (int)n, eps2, v, pot, workspace,
+                                                    st);
+    if (e == hipSuccess) e = hipEventRecord(ev[3 * r + 1], st);
+    if (e == hipSuccess && !one_sided)
+      e = nbody::launch_symmetric_reduce((int)n, G, accel_out, v, pot, workspace, st);
+    if (e == hipSuccess) e = hipEventRecord(ev[3 * r + 2], st);
+  }
+  if (e == hipSuccess) e = hipEventSynchronize(ev.back());
+  for (int r = 0; r < reps && e == hipSuccess; ++r) {
+    e = hipEventElapsedTime(&pass_ms[r], ev[3 * r], ev[3 * r + 2]);
+    if (e == hipSuccess && kernel_ms)
+      e = hipEventElapsedTime(&kernel_ms[r], ev[3 * r], ev[3 * r + 1]);
+  }
+  destroy_events(ev);
+  return hip_status(e);
 }
 
 }  // extern "C"

@@ -21,6 +21,8 @@
  *    frees, copies to the host or synchronises; every call only enqueues
  *    kernels on `stream` (a hipStream_t passed as void*; NULL = the null
  *    stream) and returns.  Results are ready when the stream reaches them.
+ *    The timing calls at the end of this header are the exception: they
+ *    create HIP events and wait for them.
  *  - float4 arrays are float[n][4], 16-byte aligned; float3 arrays are
  *    float[n][3] and plain float arrays float[n], 4-byte aligned.
  *  - n is the body count: 0 <= n <= NBODY_MAX_N.  n == 0 is a no-op that
@@ -45,7 +47,7 @@
 extern "C" {
 #endif
 
-#define NBODY_ABI_VERSION 1
+#define NBODY_ABI_VERSION 2
 
 /* Largest accepted body count (2^30).  Body indices are 32-bit inside the
  * kernels; byte offsets are 64-bit. */
@@ -108,15 +110,18 @@ int nbody_accel_variant(const float *posmass, int64_t n, float G, float eps2,
 int nbody_accel_variant_count(void);
 
 /* Describes variant v: bodies per lane, tile width T (the two-level
- * summation chunk), waves per block, j split S, and how j-bodies reach the
+ * summation chunk), waves per block, j split S, how j-bodies reach the
  * pair step (staging: 0 = LDS tiles read as wavefront broadcasts; 1 =
  * wave-uniform scalar loads into SGPRs; 2 = vector loads of one address per
- * wavefront, i.e. through the caches only).  Variants with staging != 0 are
- * an ablation of the LDS design and exist for nbody_accel_variant and
- * nbody_accel_range only.  Returns NBODY_ERR_INVALID_ARG for an unknown v;
- * any pointer may be NULL to skip that field. */
+ * wavefront, i.e. through the caches only), and the unroll factor of the
+ * inner j loop (the tunable of the CUDA Handbook's Table 14-2).  Variants
+ * with staging != 0 are an ablation of the LDS design and exist for
+ * nbody_accel_variant and nbody_accel_range only.  Returns
+ * NBODY_ERR_INVALID_ARG for an unknown v; any pointer may be NULL to skip
+ * that field. */
 int nbody_accel_variant_info(int v, int *bodies_per_lane, int *tile,
-                             int *waves_per_block, int *split, int *staging);
+                             int *waves_per_block, int *split, int *staging,
+                             int *unroll);
 
 /* The variant nbody_accel uses for n bodies. */
 int nbody_accel_variant_for_n(int64_t n);
@@ -296,7 +301,13 @@ int nbody_accel_soa(const float *x, const float *y, const float *z,
 int nbody_leapfrog_step(float *posmass, float *vel, const float *accel,
                         float dt, int64_t n, void *stream);
 
-/* Closing half-kick v <- v + h a (h = dt/2 for kick-drift-kick).
+/* Closing half-kick v <- v + h a (h = dt/2 for kick-drift-kick).  The
+ * README's section 1.3 prints one half kick and a drift per step and keeps
+ * the velocities at half steps; this library reads the scheme as standard
+ * kick-drift-kick leapfrog, so that the velocities are synchronised with
+ * the positions after every step (and energy is defined there): the step is
+ * nbody_leapfrog_step (the printed two updates), a force pass at the new
+ * positions, then this second half kick with the new accelerations.
  *   vel [n] float4 in place (w unchanged); accel [n] float4, disjoint. */
 int nbody_kick(float *vel, const float *accel, float h, int64_t n,
                void *stream);
@@ -331,6 +342,55 @@ int nbody_energy_from_potential(const float *posmass, const float *vel,
                                 void *workspace, size_t workspace_bytes,
                                 double *stats_out, void *stream);
 size_t nbody_energy_from_potential_workspace_bytes(int64_t n);
+
+/* ---------------------------------------------------------------------------
+ * Timing, for benchmarks.  HIP events created by the library and recorded
+ * on the stream the timed work is launched on: the event-timing pattern of
+ * the atomics tutorial ("CUDA programming (9)", its timing() helper: record
+ * an event, run the work, record a second event, wait for it, read the
+ * elapsed time), repeated over several runs.  These calls, unlike the rest
+ * of the library, create and destroy HIP events, and nbody_time_accel and
+ * nbody_timer_elapsed_ms wait for the GPU; none of them may be used while
+ * the stream is being captured into a graph (NBODY_ERR_INVALID_ARG).  The
+ * stream must belong to the current HIP device.
+ * ------------------------------------------------------------------------- */
+
+/* An opaque set of HIP events ("marks") for bracketing work on streams. */
+typedef struct nbody_timer nbody_timer;
+
+/* Creates a timer of `marks` events (1 <= marks <= 1 << 20). */
+int nbody_timer_create(int marks, nbody_timer **timer_out);
+/* Records event `mark` on `stream` (a later call re-records it). */
+int nbody_timer_mark(nbody_timer *timer, int mark, void *stream);
+/* Waits for event `to` and writes the time from event `from` to event `to`
+ * in milliseconds.  NBODY_ERR_HIP if either was never recorded. */
+int nbody_timer_elapsed_ms(nbody_timer *timer, int from, int to, float *ms_out);
+/* Destroys the timer's events and frees it (NULL is a no-op). */
+int nbody_timer_destroy(nbody_timer *timer);
+
+/* Force passes nbody_time_accel can run. */
+#define NBODY_PASS_ONE_SIDED 0            /* nbody_accel_variant; -1: nbody_accel */
+#define NBODY_PASS_SYMMETRIC 1            /* nbody_accel_symmetric */
+#define NBODY_PASS_SYMMETRIC_POTENTIAL 2  /* nbody_accel_symmetric_potential */
+
+/* Runs `reps` force passes of the given kind back to back on `stream`, each
+ * bracketed by events recorded inside the library, waits for the last, and
+ * writes the host arrays:
+ *   pass_ms[r]    duration of pass r (all of its kernels);
+ *   kernel_ms[r]  duration of its dominant kernel alone: the panel-pair
+ *                 kernel of the pair-symmetric passes (their reduce kernel
+ *                 follows it), the whole pass for the one-sided one.  May be
+ *                 NULL.
+ *   variant       as the pass's entry point (-1: the library's choice).
+ *   workspace     the pair-symmetric passes' workspace (ignored for the
+ *                 one-sided pass; may then be NULL).
+ * Other arguments, sizes and errors as the pass's entry point; additionally
+ * NBODY_ERR_INVALID_ARG for n == 0, reps < 1 or reps > 1 << 16, an unknown
+ * pass, a NULL pass_ms, or a stream being captured. */
+int nbody_time_accel(const float *posmass, int64_t n, float G, float eps2,
+                     float *accel_out, int pass, int variant, void *workspace,
+                     size_t workspace_bytes, int reps, float *pass_ms,
+                     float *kernel_ms, void *stream);
 
 #ifdef __cplusplus
 }

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.nbody_abi_version() == 1
+    assert lib.nbody_abi_version() == 2
     for code in (0, -1, -2, -3, -4, -5):
         s = nb.status_string(code)
         assert s and s != "unknown status"
@@ -49,6 +49,7 @@ def test_variant_table(lib):
     for v in range(count):
         info = nb.nbody_accel_variant_info(v)
         assert info["bodies_per_lane"] in (1, 2, 4, 8)
+        assert info["unroll"] in (1, 2, 4, 8)
         assert info["waves_per_block"] % info["split"] == 0
         assert (info["split"] * info["tile"]) % (64 * info["waves_per_block"]) == 0
     with pytest.raises(nb.NBodyError):
@@ -329,3 +330,38 @@ def test_potential_and_energy_from_potential_validation(lib):
     assert e(vp(A), vp(B), vp(C), 1000, vp(D), need, vp(D + need + 4), None) == nb.NBODY_ERR_ALIGNMENT
     assert e(vp(A), vp(B), vp(C), 1000, vp(C + 16), need, vp(D), None) == nb.NBODY_ERR_ALIAS
     assert e(vp(A), vp(B), vp(C), 1000, vp(D), need, vp(D + 8), None) == nb.NBODY_ERR_ALIAS
+
+
+def test_timing_validation(lib):
+    """nbody_time_accel and the timer calls reject bad arguments before they
+    create an event or touch the stream."""
+    f = lib.nbody_time_accel
+    ms = (ctypes.c_float * 4)()
+    INV = nb.NBODY_ERR_INVALID_ARG
+    one, sym = nb.NBODY_PASS_ONE_SIDED, nb.NBODY_PASS_SYMMETRIC
+
+    def call(n=10, G=1.0, eps2=1e-4, out=B, kind=one, v=-1, ws=None, wsb=0, reps=4, pms=ms):
+        return f(vp(A), n, G, eps2, vp(out), kind, v, ws, wsb, reps, pms, None, None)
+
+    assert call(n=0) == INV                       # nothing to time
+    assert call(reps=0) == INV
+    assert call(reps=(1 << 16) + 1) == INV
+    assert call(kind=3) == INV
+    assert call(kind=-1) == INV
+    assert call(pms=None) == INV
+    assert call(eps2=0.0) == INV                  # the pass's own checks
+    assert call(v=10 ** 6) == INV
+    assert call(out=A) == nb.NBODY_ERR_ALIAS
+    assert call(out=B + 8) == nb.NBODY_ERR_ALIGNMENT
+    assert call(kind=sym) == nb.NBODY_ERR_WORKSPACE
+    need = nb.nbody_accel_symmetric_workspace_bytes(10)
+    assert call(kind=sym, ws=vp(C), wsb=need - 1) == nb.NBODY_ERR_WORKSPACE
+    assert call(kind=sym, ws=vp(A), wsb=need) == nb.NBODY_ERR_ALIAS
+    t = vp()
+    assert lib.nbody_timer_create(0, ctypes.byref(t)) == INV
+    assert lib.nbody_timer_create((1 << 20) + 1, ctypes.byref(t)) == INV
+    assert lib.nbody_timer_create(4, None) == INV
+    assert lib.nbody_timer_mark(None, 0, None) == INV
+    out = ctypes.c_float()
+    assert lib.nbody_timer_elapsed_ms(None, 0, 1, ctypes.byref(out)) == INV
+    assert lib.nbody_timer_destroy(None) == nb.NBODY_OK

@@ -110,25 +110,46 @@ def test_energy_deterministic():
     assert a == b
 
 
-def run_kdk(pm_np, vel_np, G, eps2, dt, steps, check_every=None):
+# The two force passes a kick-drift-kick step can use: the one-sided
+# nbody_accel, and the pair-symmetric nbody_accel_symmetric (the library's
+# variant for n, the pass bench.py times at 2^20 bodies).
+FORCE_PATHS = ("one_sided", "symmetric")
+
+
+def force_pass(path, n):
+    """None (nb.kdk_step's default, nbody_accel) or a SymmetricPass for n."""
+    return None if path == "one_sided" else nb.SymmetricPass(n, DEV)
+
+
+def accel_with(force, pm, G, eps2, acc):
+    if force is None:
+        nb.nbody_accel(pm, G, eps2, acc)
+    else:
+        force(pm, G, eps2, acc)
+
+
+def run_kdk(pm_np, vel_np, G, eps2, dt, steps, check_every=None, path="one_sided"):
     pm, vel = to_dev(pm_np), to_dev(vel_np)
     acc = torch.empty_like(pm)
-    nb.nbody_accel(pm, G, eps2, acc)
+    force = force_pass(path, pm.shape[0])
+    accel_with(force, pm, G, eps2, acc)
     energies = [nb.energy(pm, vel, G, eps2)]
     for s in range(steps):
-        nb.kdk_step(pm, vel, acc, G, eps2, dt)
+        nb.kdk_step(pm, vel, acc, G, eps2, dt, force=force)
         if check_every and (s + 1) % check_every == 0:
             energies.append(nb.energy(pm, vel, G, eps2))
     torch.cuda.synchronize()
     return pm, vel, acc, energies
 
 
-def test_plummer16k_ten_steps():
+@pytest.mark.parametrize("path", FORCE_PATHS)
+def test_plummer16k_ten_steps(path):
     w = workloads.WORKLOADS["plummer16k"]
     pm0, v0 = workloads.make("plummer16k")
-    pm, vel, acc, es = run_kdk(pm0, v0, w.G, w.eps2, w.dt, w.steps, check_every=w.steps)
+    pm, vel, acc, es = run_kdk(pm0, v0, w.G, w.eps2, w.dt, w.steps, check_every=w.steps,
+                               path=path)
     drift = abs(es[-1]["E"] - es[0]["E"]) / abs(es[0]["E"])
-    log(f"plummer16k energy drift {drift:.3e}")
+    log(f"plummer16k ({path}) energy drift {drift:.3e}")
     assert drift <= 1e-4
     pm_np = pm.cpu().numpy()
     assert np.array_equal(pm_np[:, 3], pm0[:, 3])
@@ -142,16 +163,16 @@ def test_plummer16k_ten_steps():
     pm10 = np.concatenate([x_ref.astype(F32), pm0[:, 3:4]], axis=1)
     t10 = to_dev(pm10)
     a10 = torch.empty_like(t10)
-    nb.nbody_accel(t10, w.G, w.eps2, a10)
+    accel_with(force_pass(path, w.n), t10, w.G, w.eps2, a10)
     torch.cuda.synchronize()
     pos10, mass10 = oracle.split_posmass(pm10)
     assert_parity(a10.cpu().numpy(), oracle.accel(pos10, mass10, w.G, float(F32(w.eps2))),
-                  "plummer16k step-10 state")
+                  f"plummer16k step-10 state ({path})")
     # the GPU run's own step-10 accelerations against the oracle run's: the
     # states differ by the trajectory error checked below, so only the
     # relative L2 bar is asserted; the worst body is reported
     l2, worst = errors(acc.cpu().numpy(), a_ref)
-    log(f"plummer16k step 10: GPU run's accel vs oracle run's accel, rel L2 {l2:.2e}, "
+    log(f"plummer16k step 10 ({path}): GPU run's accel vs oracle run's accel, rel L2 {l2:.2e}, "
         f"worst body {worst:.2e}")
     assert l2 <= 1e-5
     # ten fp32 drifts round x ten times (~0.5 ulp each), so the bound scales
@@ -164,36 +185,42 @@ def test_plummer16k_ten_steps():
     assert np.all(dv <= 2e-6 * (np.abs(v_ref) + 1.0))
 
 
-def test_time_reversibility():
+@pytest.mark.parametrize("path", FORCE_PATHS)
+def test_time_reversibility(path):
     pm0, v0 = workloads.plummer(4096, seed=8)
     G, eps2, dt = 1.0, 1e-4, 1e-3
-    pm, vel, acc, _ = run_kdk(pm0, v0, G, eps2, dt, 10)
+    pm, vel, acc, _ = run_kdk(pm0, v0, G, eps2, dt, 10, path=path)
     vel[:, :3] = -vel[:, :3]
-    nb.nbody_accel(pm, G, eps2, acc)
+    force = force_pass(path, pm.shape[0])
+    accel_with(force, pm, G, eps2, acc)
     for _ in range(10):
-        nb.kdk_step(pm, vel, acc, G, eps2, dt)
+        nb.kdk_step(pm, vel, acc, G, eps2, dt, force=force)
     torch.cuda.synchronize()
     x0 = pm0[:, :3].astype(np.float64)
     dx = np.abs(pm.cpu().numpy()[:, :3] - x0)
     dv = np.abs(-vel.cpu().numpy()[:, :3] - v0[:, :3])
-    log(f"reversibility: max |dx|/(|x|+1) {(dx / (np.abs(x0) + 1)).max():.2e}, max |dv| {dv.max():.2e}")
+    log(f"reversibility ({path}): max |dx|/(|x|+1) {(dx / (np.abs(x0) + 1)).max():.2e}, "
+        f"max |dv| {dv.max():.2e}")
     assert np.all(dx <= 4e-6 * (np.abs(x0) + 1.0))
     assert dv.max() <= 1e-5
 
 
-def test_collision1m_twenty_steps():
+@pytest.mark.parametrize("path", FORCE_PATHS)
+def test_collision1m_twenty_steps(path):
     """Two Plummer spheres, N = 1000003, 20 KDK steps of dt = 1e-3:
     momentum change <= 1e-6, relative energy drift <= 1e-3, and Newton's third
     law on the final accelerations (the oracle cannot integrate 10^6 bodies in
-    a test's time; step-0 parity is test_collision1m_ragged_sampled)."""
+    a test's time; step-0 parity over every body is in
+    test_gpu_parity_full.py)."""
     w = workloads.WORKLOADS["collision1m"]
     pm0, v0 = workloads.make("collision1m")
-    log("collision1m: integrating")
-    pm, vel, acc, es = run_kdk(pm0, v0, w.G, w.eps2, w.dt, w.steps, check_every=w.steps)
+    log(f"collision1m ({path}): integrating")
+    pm, vel, acc, es = run_kdk(pm0, v0, w.G, w.eps2, w.dt, w.steps, check_every=w.steps,
+                               path=path)
     e0, e1 = es[0], es[-1]
     dp = math.sqrt(sum((e1[k] - e0[k]) ** 2 for k in ("Px", "Py", "Pz")))
     drift = abs(e1["E"] - e0["E"]) / abs(e0["E"])
-    log(f"collision1m: |dP| {dp:.3e}, energy drift {drift:.3e}")
+    log(f"collision1m ({path}): |dP| {dp:.3e}, energy drift {drift:.3e}")
     assert dp <= 1e-6
     assert drift <= 1e-3
     pm_np = pm.cpu().numpy()
@@ -201,7 +228,7 @@ def test_collision1m_twenty_steps():
     a = acc.cpu().numpy()[:, :3].astype(np.float64)
     m = pm_np[:, 3:4].astype(np.float64)
     newton = np.linalg.norm((m * a).sum(axis=0)) / (m[:, 0] * np.linalg.norm(a, axis=1)).sum()
-    log(f"collision1m step 20: |sum m a| / sum m|a| = {newton:.2e}")
+    log(f"collision1m ({path}) step 20: |sum m a| / sum m|a| = {newton:.2e}")
     assert newton <= 1e-6
     assert np.all(a[:, :3] == a[:, :3])          # no NaN
 
@@ -363,7 +390,8 @@ def test_symmetric_potential_plummer1m_sampled():
     check_potential(a, pm, w.G, w.eps2, rows, "plummer1m")
 
 
-def test_circular_binary_one_orbit():
+@pytest.mark.parametrize("path", FORCE_PATHS)
+def test_circular_binary_one_orbit(path):
     """Equal-mass circular binary (d = 1, eps^2 = 1e-4, omega^2 = G (m1 + m2) /
     (d^2 + eps^2)^{3/2}) for one period at dt = T/1000 with the GPU's KDK
     step: the separation stays within (omega dt)^2 plus float32 rounding of d,
@@ -378,16 +406,17 @@ def test_circular_binary_one_orbit():
     v0 = np.array([[0, -omega * 0.5, 0, 0], [0, omega * 0.5, 0, 0]], F32)
     pm, vel = to_dev(pm0), to_dev(v0)
     acc = torch.empty_like(pm)
-    nb.nbody_accel(pm, 1.0, eps2, acc)
+    force = force_pass(path, 2)
+    accel_with(force, pm, 1.0, eps2, acc)
     worst = 0.0
     for k in range(steps):
-        nb.kdk_step(pm, vel, acc, 1.0, eps2, dt)
+        nb.kdk_step(pm, vel, acc, 1.0, eps2, dt, force=force)
         if (k + 1) % 50 == 0:
             x = pm.cpu().numpy()[:, :3].astype(np.float64)
             worst = max(worst, abs(np.linalg.norm(x[1] - x[0]) - 1.0))
     torch.cuda.synchronize()
     x = pm.cpu().numpy()[:, :3].astype(np.float64)
-    log(f"circular binary: max |d - 1| {worst:.2e} (bound {(omega * dt) ** 2:.2e}), "
+    log(f"circular binary ({path}): max |d - 1| {worst:.2e} (bound {(omega * dt) ** 2:.2e}), "
         f"return error {np.abs(x - pm0[:, :3]).max():.2e}")
     assert worst <= (omega * dt) ** 2 + 1e-5
     assert np.abs(x - pm0[:, :3]).max() <= 2e-3
