@@ -27,6 +27,7 @@ NBODY_ERR_ALIAS = -3
 NBODY_ERR_WORKSPACE = -4
 NBODY_ERR_HIP = -5
 NBODY_MAX_N = 1 << 30
+NBODY_ENERGY_STATIC_SCRATCH_BYTES = 16 << 20
 
 # Every symbol include/nbody.h declares.
 EXPORTS = (
@@ -46,7 +47,7 @@ EXPORTS = (
     "nbody_accel_symmetric_potential_variant_for_n",
     "nbody_accel_f3aos", "nbody_accel_soa",
     "nbody_leapfrog_step", "nbody_kick",
-    "nbody_energy", "nbody_energy_workspace_bytes",
+    "nbody_energy", "nbody_energy_workspace_bytes", "nbody_energy_static",
     "nbody_timer_create", "nbody_timer_mark", "nbody_timer_elapsed_ms", "nbody_timer_destroy",
     "nbody_time_accel",
 )
@@ -118,6 +119,7 @@ def load_library(path: str | None = None):
         "nbody_kick": (c_int, [vp, vp, c_f, c_i64, vp]),
         "nbody_energy": (c_int, [vp, vp, c_i64, c_f, c_f, vp, c_sz, vp, vp]),
         "nbody_energy_workspace_bytes": (c_sz, [c_i64]),
+        "nbody_energy_static": (c_int, [vp, vp, c_i64, c_f, c_f, vp, vp]),
         "nbody_timer_create": (c_int, [c_int, ctypes.POINTER(vp)]),
         "nbody_timer_mark": (c_int, [vp, c_int, vp]),
         "nbody_timer_elapsed_ms": (c_int, [vp, c_int, c_int, ctypes.POINTER(c_f)]),
@@ -509,6 +511,22 @@ def nbody_time_accel(posmass, G: float, eps2: float, accel_out, pass_kind: int, 
                                            kernel_ms, _stream(stream)),
            "nbody_time_accel")
     return list(pass_ms)[:reps], list(kernel_ms)[:reps]
+
+
+def nbody_energy_static(posmass, vel, G: float, eps2: float, stats_out, stream=None):
+    """nbody_energy with the library's static device scratch (no workspace):
+    stats_out float64 [8] GPU tensor <- {K, W, E, Px, Py, Pz, M, 0}."""
+    torch = _torch()
+    n = _n_of(posmass)
+    if _n_of(vel) != n:
+        raise ValueError("posmass and vel must have N rows")
+    if stats_out.numel() < 8:
+        raise ValueError("stats_out needs 8 doubles")
+    _check(load_library().nbody_energy_static(_f32(posmass, "posmass", (4,)),
+                                              _f32(vel, "vel", (4,)), n, G, eps2,
+                                              _dev(stats_out, "stats_out", None, torch.float64),
+                                              _stream(stream)),
+           "nbody_energy_static")
 
 
 # ---------------------------------------------------------------------------

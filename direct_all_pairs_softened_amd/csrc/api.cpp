@@ -11,6 +11,9 @@
 
 #include "nbody_internal.hpp"
 
+static_assert(NBODY_ENERGY_STATIC_SCRATCH_BYTES == nbody::kEnergyStaticScratchBytes,
+              "the header's scratch size must match the library's");
+
 namespace {
 
 using nbody::BodyArrays;
@@ -416,6 +419,26 @@ int nbody_energy_from_potential(const float *posmass, const float *vel, const fl
   if (overlap(workspace, need, stats_out, sb)) return NBODY_ERR_ALIAS;
   return hip_status(nbody::launch_energy_from_potential(posmass, vel, accel_pot, (int)n, workspace,
                                                         stats_out, as_stream(stream)));
+}
+
+int nbody_energy_static(const float *posmass, const float *vel, int64_t n, float G, float eps2,
+                        double *stats_out, void *stream) {
+  if (!n_ok(n)) return NBODY_ERR_INVALID_ARG;
+  if (int s = check_consts(G, eps2)) return s;
+  if (n == 0) return NBODY_OK;  // stats_out is left untouched
+  if (nbody::energy_pair_tasks(n) > INT32_MAX - 8) return NBODY_ERR_INVALID_ARG;
+  if (!posmass || !vel || !stats_out) return NBODY_ERR_INVALID_ARG;
+  if (!aligned(stats_out, 8)) return NBODY_ERR_ALIGNMENT;
+  if (!aligned(posmass, 16) || !aligned(vel, 16)) return NBODY_ERR_ALIGNMENT;
+  if (nbody::energy_workspace_bytes(n) > NBODY_ENERGY_STATIC_SCRATCH_BYTES)
+    return NBODY_ERR_WORKSPACE;
+  const size_t bytes = (size_t)n * 16, sb = 8 * sizeof(double);
+  if (overlap(stats_out, sb, posmass, bytes) || overlap(stats_out, sb, vel, bytes))
+    return NBODY_ERR_ALIAS;
+  void *scratch = nullptr;
+  if (nbody::energy_static_scratch(&scratch) != hipSuccess) return NBODY_ERR_HIP;
+  return hip_status(nbody::launch_energy(posmass, vel, (int)n, G, eps2, scratch, stats_out,
+                                         as_stream(stream)));
 }
 
 size_t nbody_energy_workspace_bytes(int64_t n) {

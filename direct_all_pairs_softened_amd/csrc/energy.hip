@@ -23,6 +23,8 @@
 #include "nbody_common.hpp"
 #include "nbody_internal.hpp"
 
+#include <mutex>
+
 namespace nbody {
 
 namespace {
@@ -231,6 +233,36 @@ size_t energy_workspace_bytes(int64_t n) {
 }
 
 int64_t energy_pair_tasks(int64_t n) { return n <= 0 ? 0 : pair_tasks(n); }
+
+// Scratch of the allocation-free energy entry point: one copy per GPU, held
+// until the process ends.  Host code never uses this name as an address (on
+// the host it is only a stand-in for the symbol); it uses the device address
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[kEnergyStaticScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+hipError_t energy_static_scratch(void **ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_energy(const float *posmass, const float *vel, int n, float G, float eps2,
                          void *workspace, double *stats, hipStream_t stream) {

@@ -90,5 +90,9 @@ hipError_t launch_energy_from_potential(const float *posmass, const float *vel,
                                         double *stats, hipStream_t stream);
 hipError_t launch_energy(const float *posmass, const float *vel, int n, float G, float eps2,
                          void *workspace, double *stats, hipStream_t stream);
+// The allocation-free energy entry point's static device scratch: its size,
+// and its device address on the current GPU (looked up once per GPU).
+constexpr size_t kEnergyStaticScratchBytes = (size_t)16 << 20;
+hipError_t energy_static_scratch(void **ptr);
 
 }  // namespace nbody

@@ -331,6 +331,29 @@ int nbody_energy(const float *posmass, const float *vel, int64_t n, float G,
 
 size_t nbody_energy_workspace_bytes(int64_t n);
 
+/* nbody_energy without a caller workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving or simulation
+ * loops, harnesses that forbid hipMalloc.  The same kernels and the same
+ * fixed summation order as nbody_energy, so stats_out is bitwise equal to
+ * nbody_energy's for the same inputs.  Their scratch (per-block and per
+ * panel-pair fp64 partial sums, nbody_energy_workspace_bytes(n) bytes) is a
+ * static device array of NBODY_ENERGY_STATIC_SCRATCH_BYTES inside the
+ * library, one per GPU, held until the process ends; its device address is
+ * looked up once per GPU, on the first call made with that GPU current.
+ * Nothing in it needs to start at zero: every call writes each partial it
+ * reads.  The call allocates nothing and frees nothing.
+ *   n          0 <= n, with nbody_energy_workspace_bytes(n) <=
+ *              NBODY_ENERGY_STATIC_SCRATCH_BYTES, i.e. n <= 4,063,232;
+ *              larger n is NBODY_ERR_WORKSPACE.
+ *   stream     must belong to the current HIP device.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap on one
+ * GPU (on different streams, or from different host threads) race on it and
+ * must be ordered by the caller.  Other arguments and errors as
+ * nbody_energy. */
+#define NBODY_ENERGY_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+int nbody_energy_static(const float *posmass, const float *vel, int64_t n, float G,
+                        float eps2, double *stats_out, void *stream);
+
 /* Energy and momentum in O(n) from the potentials nbody_accel_potential or
  * nbody_accel_symmetric_potential stored in accel_pot[i].w: stats_out = {K, W, K + W, Px, Py, Pz, M, 0}
  * with W = sum_i m_i Phi_i / 2 (each pair once).  fp64 fixed-order

@@ -365,3 +365,23 @@ def test_timing_validation(lib):
     out = ctypes.c_float()
     assert lib.nbody_timer_elapsed_ms(None, 0, 1, ctypes.byref(out)) == INV
     assert lib.nbody_timer_destroy(None) == nb.NBODY_OK
+
+
+def test_energy_static_validation(lib):
+    """The allocation-free energy entry point checks its arguments, and that
+    n fits its static scratch, before it looks up the scratch's address."""
+    f = lib.nbody_energy_static
+    INV = nb.NBODY_ERR_INVALID_ARG
+    assert f(vp(A), vp(B), 0, 1.0, 1e-4, vp(C), None) == nb.NBODY_OK        # n == 0: no-op
+    assert f(None, vp(B), 10, 1.0, 1e-4, vp(C), None) == INV
+    assert f(vp(A), vp(B), 10, 1.0, 1e-4, None, None) == INV
+    assert f(vp(A), vp(B), 10, 1.0, 0.0, vp(C), None) == INV
+    assert f(vp(A), vp(B), -1, 1.0, 1e-4, vp(C), None) == INV
+    assert f(vp(A + 4), vp(B), 10, 1.0, 1e-4, vp(C), None) == nb.NBODY_ERR_ALIGNMENT
+    assert f(vp(A), vp(B), 10, 1.0, 1e-4, vp(C + 4), None) == nb.NBODY_ERR_ALIGNMENT
+    assert f(vp(A), vp(B), 10, 1.0, 1e-4, vp(A + 32), None) == nb.NBODY_ERR_ALIAS
+    nmax = 4_063_232
+    assert nb.nbody_energy_workspace_bytes(nmax) <= nb.NBODY_ENERGY_STATIC_SCRATCH_BYTES
+    assert nb.nbody_energy_workspace_bytes(nmax + 1) > nb.NBODY_ENERGY_STATIC_SCRATCH_BYTES
+    assert f(vp(A), vp(B), nmax + 1, 1.0, 1e-4, vp(C), None) == nb.NBODY_ERR_WORKSPACE
+    assert f(vp(A), vp(B), 10 ** 7, 1.0, 1e-4, vp(C), None) == nb.NBODY_ERR_WORKSPACE
