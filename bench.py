@@ -336,9 +336,13 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="plummer1m")
-    ap.add_argument("--path", choices=("tile", "symmetric"), default="symmetric",
-                    help="force pass: one-sided LDS-tiled (nbody_accel) or pair-symmetric "
-                         "(nbody_accel_symmetric)")
+    ap.add_argument("--path", choices=("tile", "symmetric", "symmetric_chunked"),
+                    default="symmetric",
+                    help="force pass: one-sided LDS-tiled (nbody_accel), pair-symmetric "
+                         "(nbody_accel_symmetric), or pair-symmetric in column chunks "
+                         "(nbody_accel_symmetric_chunked)")
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="panels per chunk for --path symmetric_chunked (0: the library's)")
     ap.add_argument("--variant", type=int, default=None, help="force a compiled force variant")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target length of the oracle CPU-baseline sample")
@@ -409,6 +413,21 @@ def main():
 
         def force_rest():
             nb.nbody_accel_symmetric_reduce(w.n, w.G, acc, sym_ws, variant)
+    elif args.path == "symmetric_chunked":
+        variant = (args.variant if args.variant is not None
+                   else nb.nbody_accel_symmetric_variant_for_n(w.n))
+        ws_bytes = nb.nbody_accel_symmetric_chunked_workspace_bytes(w.n, variant, args.chunk)
+        sym_ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        info = {"path": "symmetric_chunked", "panel": nb.nbody_accel_symmetric_panel(variant),
+                "chunk_panels": args.chunk or 32, "workspace_bytes": ws_bytes}
+
+        # every chunk's panel-pair and reduce kernels: the events bracket the
+        # whole pass
+        def force_main():
+            nb.nbody_accel_symmetric_chunked(pm, w.G, w.eps2, acc, sym_ws, variant, args.chunk)
+
+        def force_rest():
+            pass
     else:
         variant = args.variant if args.variant is not None else nb.nbody_accel_variant_for_n(w.n)
         info = dict(nb.nbody_accel_variant_info(variant), path="tile")
@@ -472,7 +491,7 @@ def main():
     # the one-sided pass (nbody_accel, no workspace) on the same positions, for
     # comparison
     one_ms = None
-    if args.path == "symmetric" and not args.no_one_sided:
+    if args.path != "tile" and not args.no_one_sided:
         one_ms, _ = nb.nbody_time_accel(pm, w.G, w.eps2, acc, nb.NBODY_PASS_ONE_SIDED, 2)
         log(f"one-sided nbody_accel: {min(one_ms):.3f} ms")
 
@@ -481,7 +500,7 @@ def main():
     stats = torch.zeros(8, dtype=torch.float64, device=dev)
     energy_ms = _time(nb, lambda: nb.nbody_energy(pm, vel, w.G, w.eps2, ws, stats), 1)[0]
     checkpoint_ms = None
-    if args.path == "symmetric":
+    if args.path != "tile":
         # a checkpoint step's force pass with the potentials in accel.w, then
         # the O(N) energy from them (in place of force pass + energy pass)
         pv = nb.nbody_accel_symmetric_potential_variant_for_n(w.n)
@@ -501,7 +520,7 @@ def main():
     # counted interaction: the pair-symmetric step evaluates each pair once
     # for two interactions (3 sub, 1 fma, 2 fmac, 4 mul, 6 fmac = 25 flops),
     # the one-sided step 3 sub, 3 fma, 3 mul, 3 fmac = 18 flops
-    issued = 12.5 if args.path == "symmetric" else 18.0
+    issued = 18.0 if args.path == "tile" else 12.5
     traffic = traffic_per_launch(args.path, variant, w.name)
     out = {
         "metric": METRIC,
@@ -531,7 +550,7 @@ def main():
         "force_ms": force_avg,
         "force_kernel_ms": kernel_avg,
         "force_pass_frac": pass_tflops / PEAK_FP32_TFLOPS,
-        "pairs_evaluated_per_interaction": 0.5 if args.path == "symmetric" else 1.0,
+        "pairs_evaluated_per_interaction": 1.0 if args.path == "tile" else 0.5,
         "fp32_flops_issued_per_interaction": issued,
         "fp32_issued_frac": issued * inter / (kernel_avg * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
         "one_sided_force_ms": min(one_ms) if one_ms else None,

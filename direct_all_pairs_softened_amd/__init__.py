@@ -42,6 +42,7 @@ EXPORTS = (
     "nbody_accel_symmetric_variant_count", "nbody_accel_symmetric_panel",
     "nbody_accel_symmetric_variant_for_n",
     "nbody_accel_symmetric_tasks", "nbody_accel_symmetric_reduce",
+    "nbody_accel_symmetric_chunked", "nbody_accel_symmetric_chunked_workspace_bytes",
     "nbody_accel_symmetric_potential", "nbody_accel_symmetric_potential_workspace_bytes",
     "nbody_accel_symmetric_potential_variant_count", "nbody_accel_symmetric_potential_panel",
     "nbody_accel_symmetric_potential_variant_for_n",
@@ -106,6 +107,9 @@ def load_library(path: str | None = None):
         "nbody_accel_symmetric_panel": (c_int, [c_int]),
         "nbody_accel_symmetric_variant_for_n": (c_int, [c_i64]),
         "nbody_accel_symmetric_tasks": (c_int, [vp, c_i64, c_f, c_int, vp, c_sz, vp]),
+        "nbody_accel_symmetric_chunked": (c_int, [vp, c_i64, c_f, c_f, vp, c_int, c_int, vp,
+                                                  c_sz, vp]),
+        "nbody_accel_symmetric_chunked_workspace_bytes": (c_sz, [c_i64, c_int, c_int]),
         "nbody_accel_symmetric_reduce": (c_int, [c_i64, c_f, vp, c_int, vp, c_sz, vp]),
         "nbody_accel_symmetric_potential": (c_int, [vp, c_i64, c_f, c_f, vp, c_int, vp, c_sz,
                                                     vp]),
@@ -333,6 +337,28 @@ def nbody_accel_symmetric(posmass, G: float, eps2: float, accel_out, workspace,
                                                 _f32(accel_out, "accel_out", (4,)),
                                                 int(variant), ws, nbytes, _stream(stream)),
            "nbody_accel_symmetric")
+
+
+def nbody_accel_symmetric_chunked_workspace_bytes(n: int, variant: int = -1,
+                                                  chunk_panels: int = 0) -> int:
+    return int(load_library().nbody_accel_symmetric_chunked_workspace_bytes(
+        int(n), int(variant), int(chunk_panels)))
+
+
+def nbody_accel_symmetric_chunked(posmass, G: float, eps2: float, accel_out, workspace,
+                                  variant: int = -1, chunk_panels: int = 0, stream=None):
+    """Pair-symmetric force pass in column chunks (bitwise equal to
+    nbody_accel_symmetric); workspace: a GPU tensor of at least
+    nbody_accel_symmetric_chunked_workspace_bytes(N, variant, chunk_panels) bytes."""
+    n = _n_of(posmass)
+    if _n_of(accel_out) != n:
+        raise ValueError("accel_out must have N rows")
+    ws = _dev(workspace, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(load_library().nbody_accel_symmetric_chunked(
+        _f32(posmass, "posmass", (4,)), n, G, eps2, _f32(accel_out, "accel_out", (4,)),
+        int(variant), int(chunk_panels), ws, nbytes, _stream(stream)),
+        "nbody_accel_symmetric_chunked")
 
 
 def nbody_accel_symmetric_tasks(posmass, eps2: float, workspace, variant: int = -1, stream=None):

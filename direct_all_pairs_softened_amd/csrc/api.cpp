@@ -266,7 +266,8 @@ static size_t sym_workspace_bytes(int64_t n, int variant, bool pot) {
 // or want_out false.  NBODY_OK with n == 0 means there is nothing to launch.
 static int sym_check(const float *posmass, int64_t n, float G, float eps2,
                      const float *accel_out, int v, bool pot, const void *workspace,
-                     size_t workspace_bytes, bool want_pm, bool want_out) {
+                     size_t workspace_bytes, bool want_pm, bool want_out,
+                     int chunk_panels = 0) {
   if (!n_ok(n)) return NBODY_ERR_INVALID_ARG;
   if (int s = check_consts(G, eps2)) return s;
   if (v >= nbody::symmetric_variant_count(pot)) return NBODY_ERR_INVALID_ARG;
@@ -277,7 +278,9 @@ static int sym_check(const float *posmass, int64_t n, float G, float eps2,
   if ((want_pm && !posmass) || (want_out && !accel_out)) return NBODY_ERR_INVALID_ARG;
   if ((want_pm && !aligned(posmass, 16)) || (want_out && !aligned(accel_out, 16)))
     return NBODY_ERR_ALIGNMENT;
-  const size_t need = nbody::symmetric_workspace_bytes(n, v, pot);
+  const size_t need = chunk_panels > 0
+                          ? nbody::symmetric_chunked_workspace_bytes(n, v, pot, chunk_panels)
+                          : nbody::symmetric_workspace_bytes(n, v, pot);
   if (!workspace || workspace_bytes < need) return NBODY_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return NBODY_ERR_ALIGNMENT;
   const size_t bytes = (size_t)n * 16;
@@ -321,6 +324,32 @@ int nbody_accel_symmetric(const float *posmass, int64_t n, float G, float eps2,
                           size_t workspace_bytes, void *stream) {
   return sym_pass(posmass, n, G, eps2, accel_out, variant, false, workspace, workspace_bytes,
                   stream);
+}
+
+static int chunk_of(int chunk_panels) {
+  return chunk_panels == 0 ? NBODY_SYMMETRIC_DEFAULT_CHUNK : chunk_panels;
+}
+
+size_t nbody_accel_symmetric_chunked_workspace_bytes(int64_t n, int variant, int chunk_panels) {
+  const int v = sym_variant(variant, n, false);
+  if (!n_ok(n) || v >= nbody::symmetric_variant_count(false) ||
+      !nbody::symmetric_chunk_ok(chunk_of(chunk_panels)))
+    return 0;
+  return nbody::symmetric_chunked_workspace_bytes(n, v, false, chunk_of(chunk_panels));
+}
+
+int nbody_accel_symmetric_chunked(const float *posmass, int64_t n, float G, float eps2,
+                                  float *accel_out, int variant, int chunk_panels,
+                                  void *workspace, size_t workspace_bytes, void *stream) {
+  const int v = sym_variant(variant, n, false);
+  const int c = chunk_of(chunk_panels);
+  if (!nbody::symmetric_chunk_ok(c)) return NBODY_ERR_INVALID_ARG;
+  if (int s = sym_check(posmass, n, G, eps2, accel_out, v, false, workspace, workspace_bytes,
+                        true, true, c))
+    return s;
+  if (n == 0) return NBODY_OK;
+  return hip_status(nbody::launch_symmetric_chunked(posmass, (int)n, G, eps2, accel_out, v,
+                                                    false, c, workspace, as_stream(stream)));
 }
 
 int nbody_accel_symmetric_tasks(const float *posmass, int64_t n, float eps2, int variant,

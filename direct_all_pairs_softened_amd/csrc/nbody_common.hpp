@@ -87,29 +87,42 @@ __host__ __device__ inline long long tri_root(long long t) {
 // each, J-major), then the triangle of the diagonal tile.  A stretch of
 // consecutive numbers therefore touches about S + stretch / S panels.
 //
+// A launch may take a contiguous range of the numbers, [t0, t0 + pairs): a
+// range of whole tile columns is the set of pairs with J in a range of
+// panels, which is how the pair-symmetric pass is cut into column chunks.
+//
 // Blocks go to the 8 XCDs of the chip round robin (block b to XCD b % 8), so
-// block b takes pair number (b % 8) * per_xcd + b / 8: each XCD walks its
-// own contiguous stretch of the order, and the panels its concurrent blocks
-// read stay in that XCD's L2.  Which block computes a pair does not change
-// any sum: every pair writes its own workspace slot.
+// block b takes pair number t0 + (b % 8) * per_xcd + b / 8: each XCD walks
+// its own contiguous stretch of the order, and the panels its concurrent
+// blocks read stay in that XCD's L2.  Which block computes a pair does not
+// change any sum: every pair writes its own workspace slot.
 struct PanelOrder {
   int P;               // panels
   int S;               // tile side in panels
-  long long pairs;     // P (P + 1) / 2
+  long long t0;        // number of the launch's first pair
+  long long pairs;     // pairs in the launch (P (P + 1) / 2 for all of them)
   long long per_xcd;   // ceil(pairs / 8): grid = 8 * per_xcd blocks
 };
 
 constexpr int kXcds = 8;
 constexpr int kPanelTile = 32;
 
-inline PanelOrder panel_order(long long P) {
+// The pairs numbered [t0, t1) of P panels.
+inline PanelOrder panel_order_range(long long P, long long t0, long long t1) {
   PanelOrder o;
   o.P = (int)P;
   o.S = kPanelTile;
-  o.pairs = P * (P + 1) / 2;
+  o.t0 = t0;
+  o.pairs = t1 - t0;
   o.per_xcd = (o.pairs + kXcds - 1) / kXcds;
   return o;
 }
+
+// Every pair of P panels.
+inline PanelOrder panel_order(long long P) { return panel_order_range(P, 0, P * (P + 1) / 2); }
+
+// Number of the first pair with J >= c (c a multiple of the tile side, or P).
+__host__ __device__ inline long long first_pair_of_column(long long c) { return c * (c + 1) / 2; }
 
 // Pair number t (0 <= t < pairs) of the order above.
 __host__ __device__ inline void panel_pair_of(const PanelOrder &o, long long t, int &I, int &J) {
@@ -129,15 +142,38 @@ __host__ __device__ inline void panel_pair_of(const PanelOrder &o, long long t, 
   }
 }
 
-// The pair block b takes; false for the few blocks past the last pair.
+// The pair block b takes; false for the few blocks past the launch's last
+// pair.
 __host__ __device__ inline bool panel_pair_of_block(const PanelOrder &o, long long b, int &I,
                                                     int &J, long long &t) {
   const long long k = b / kXcds;
-  t = (b % kXcds) * o.per_xcd + k;
-  if (k >= o.per_xcd || t >= o.pairs) return false;
+  const long long u = (b % kXcds) * o.per_xcd + k;
+  if (k >= o.per_xcd || u >= o.pairs) return false;
+  t = o.t0 + u;
   panel_pair_of(o, t, I, J);
   return true;
 }
+
+// Where the pair-symmetric pass keeps panel K's sums from panel J, for a
+// launch that takes the panel pairs (I, J') with J' in [c0, c1) (a column
+// chunk; the whole pass is the chunk [0, P)):
+//  - a panel K < c0 gets one slot per column of the chunk (its i-side sums
+//    from panels c0 .. c1 - 1): slot K (c1 - c0) + (J - c0);
+//  - a panel K in [c0, c1) gets its sums from every panel J < c1 (j-side
+//    from the panels before it, its own diagonal pair, i-side from the
+//    chunk's later panels): slot c0 (c1 - c0) + (K - c0) c1 + J.
+// For either kind of panel, consecutive J have consecutive slots.  A panel
+// K >= c1 gets nothing from the chunk.  The whole pass ([0, P)) is slot
+// K P + J.
+struct SlotMap {
+  int c0, c1;
+  __host__ __device__ long long slot(int K, int J) const {
+    const long long w = c1 - c0;
+    return K < c0 ? (long long)K * w + (J - c0)
+                  : (long long)c0 * w + (long long)(K - c0) * c1 + J;
+  }
+  __host__ __device__ long long slots() const { return (long long)(c1 - c0) * (c0 + c1); }
+};
 
 // ---------------------------------------------------------------------------
 // Body loaders / storers for the three layouts.  load(j) returns (x, y, z, m);

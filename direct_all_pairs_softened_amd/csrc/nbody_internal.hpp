@@ -75,6 +75,15 @@ hipError_t launch_symmetric_tasks(const float *posmass, int n, float eps2, int v
                                   void *workspace, hipStream_t stream);
 hipError_t launch_symmetric_reduce(int n, float G, float *accel, int v, bool pot,
                                    const void *workspace, hipStream_t stream);
+// The same pass in column chunks of chunk_panels panels (a positive multiple
+// of the panel-pair tile side, 32): per chunk a task launch and a reduce
+// launch; bitwise equal to launch_symmetric, with a workspace of one
+// chunk's slots.
+bool symmetric_chunk_ok(int chunk_panels);
+size_t symmetric_chunked_workspace_bytes(int64_t n, int v, bool pot, int chunk_panels);
+hipError_t launch_symmetric_chunked(const float *posmass, int n, float G, float eps2,
+                                    float *accel, int v, bool pot, int chunk_panels,
+                                    void *workspace, hipStream_t stream);
 
 // Integrator.
 hipError_t launch_leapfrog(float *posmass, float *vel, const float *accel, float dt, int n,

@@ -28,17 +28,28 @@
 // Diagonal tasks (I = J) use the one-sided sum (j over the whole panel,
 // self term exactly 0) and no j-side sums.
 //
-// Output of a task: part[I][J] = panel I's sums from panel J and, for I < J,
-// part[J][I] = panel J's sums from panel I.  A second kernel forms
+// Output of a task: panel I's sums from panel J and, for I < J, panel J's
+// sums from panel I, each in its own workspace slot of NC x B floats (NC = 3
+// sums per body, 4 with the potential).  A second kernel forms
 // a_i = G * sum_{J = 0 .. P-1} part[I(i)][J][i], ascending J.
-// Workspace: part float[P][P][NC][B], NC = 3 sums per body (4 with the
-// potential), i.e. 12 N^2 / B bytes (16 N^2 / B).
+// The pass runs either whole (one task launch over all P (P + 1) / 2 panel
+// pairs, slots [P][P]: 12 N^2 / B bytes) or in column chunks: a launch takes
+// the pairs with J in [c0, c1) (SlotMap gives their slots), and the chunk's
+// reduce continues each touched body's fp32 running sum (kept in accel_out
+// between chunks) in ascending J.  A body's panel sums are then added in the
+// same order as in the whole pass, so the two give bitwise equal results; the
+// chunked workspace is one chunk's slots, about 24 N C bytes for chunks of C
+// panels.
 //
 // Per pair (two interactions) a lane issues 16 FP32 VALU ops and one
 // v_rsq_f32, plus 7 / K DPP moves (rotated) or 3 / K adds (LDS-carried); the
 // one-sided kernel issues 12 ops and one v_rsq_f32 per interaction.
 #include "nbody_common.hpp"
 #include "nbody_internal.hpp"
+
+#include <algorithm>
+#include <mutex>
+#include <vector>
 
 namespace nbody {
 
@@ -108,6 +119,16 @@ __device__ __forceinline__ void sym_step(const float (&xi)[K], const float (&yi)
   }
 }
 
+// This lane's index in the wavefront, computed afresh where it is used: an
+// asm the compiler can neither merge with an earlier one nor hoist, so that
+// no lane index (or address made from one) has to be kept in a register, or
+// spilled, across the step loop of a sweep.
+__device__ __forceinline__ int fresh_lane() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // Sums kept per body: the three acceleration components, plus the potential
 // sum with POT.
 template <bool POT>
@@ -117,7 +138,7 @@ constexpr int sym_sums() {
 
 template <int K, int KP, int W, int IL, bool POT, int ML, int JL, bool DIAG>
 __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, int I, int J,
-                                         int P, float eps2, float *__restrict__ part,
+                                         SlotMap map, float eps2, float *__restrict__ part,
                                          float (*csum)[KP][sym_sums<POT>()][kWave], float *mis,
                                          float4 *jtile, float4 *jsum) {
   constexpr int B = W * kWave * K;
@@ -127,6 +148,16 @@ __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, i
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
+  // The task's two slots: panel I's sums from J, panel J's sums from I.  For
+  // 8 i-bodies per lane their addresses are formed once per task, for fewer
+  // at each use.  The addresses are the same either way; the forms differ in
+  // what the compiler keeps live across the step loop, and with it where it
+  // places each step's slot read: these are the faster forms, measured on
+  // MI355X (2^20 bodies, K = 8: 185.0 against 187.7 ms; 131072 bodies,
+  // K = 4: 3.06 against 3.13 ms).
+  constexpr bool kHoist = K >= 8;
+  float *const part_ij = part + (size_t)map.slot(I, J) * NC * B;
+  float *const part_ji = part + (size_t)map.slot(J, I) * NC * B;
 
   float xi[K], yi[K], zi[K], mi[K], ax[K], ay[K], az[K], ap[K];
 #pragma unroll
@@ -214,7 +245,10 @@ __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, i
           sum += sw[4 * l + c] + sw[4 * (l + kWave) + c];
         }
         // the force on j from i points the other way; the potential does not
-        part[(((size_t)J * P + I) * NC + c) * B + g * kWave + l] = c < 3 ? -sum : sum;
+        if constexpr (kHoist)
+          part_ji[(size_t)c * B + g * kWave + l] = c < 3 ? -sum : sum;
+        else
+          part[((size_t)map.slot(J, I) * NC + c) * B + g * kWave + l] = c < 3 ? -sum : sum;
       }
       __syncthreads();
     }
@@ -295,21 +329,33 @@ __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, i
 #pragma unroll
           for (int w = 0; w < W; ++w) sum += csum[w][p][c][l];
           // the force on j from i points the other way; the potential does not
-          part[(((size_t)J * P + I) * NC + c) * B + g * JG + p * kWave + l] = c < 3 ? -sum : sum;
+          part[((size_t)map.slot(J, I) * NC + c) * B + g * JG + p * kWave + l] = c < 3 ? -sum : sum;
         }
         __syncthreads();
       }
     }
   }
 
+  if constexpr (kHoist) {
+    const int lo = fresh_lane();
 #pragma unroll
-  for (int q = 0; q < K; ++q) {
-    const int b = wave * (kWave * K) + q * kWave + lane;
-    float *row = part + ((size_t)I * P + J) * NC * B + b;
-    row[0] = ax[q];
-    row[B] = ay[q];
-    row[2 * B] = az[q];
-    if constexpr (POT) row[3 * B] = ap[q];
+    for (int q = 0; q < K; ++q) {
+      float *row = part_ij + wave * (kWave * K) + q * kWave;
+      row[lo] = ax[q];
+      row[B + lo] = ay[q];
+      row[2 * B + lo] = az[q];
+      if constexpr (POT) row[3 * B + lo] = ap[q];
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < K; ++q) {
+      const int b = wave * (kWave * K) + q * kWave + lane;
+      float *row = part + (size_t)map.slot(I, J) * NC * B + b;
+      row[0] = ax[q];
+      row[B] = ay[q];
+      row[2 * B] = az[q];
+      if constexpr (POT) row[3 * B] = ap[q];
+    }
   }
 }
 
@@ -317,8 +363,8 @@ __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, i
 // (every XCD walks a contiguous stretch of tile-ordered pairs).
 template <int K, int KP, int W, int OCC, int IL, bool POT, int ML, int JL>
 __global__ __launch_bounds__(W *kWave) __attribute__((amdgpu_waves_per_eu(OCC))) void
-symmetric_task_kernel(const float4 *__restrict__ pm, int n, PanelOrder order, float eps2,
-                      float *__restrict__ part) {
+symmetric_task_kernel(const float4 *__restrict__ pm, int n, PanelOrder order, SlotMap map,
+                      float eps2, float *__restrict__ part) {
   constexpr int NC = sym_sums<POT>();
   __shared__ float csum[JL > 0 ? 1 : W][KP][NC][kWave];
   __shared__ float mis[ML > 0 ? W * ML * kWave : 1];
@@ -327,34 +373,55 @@ symmetric_task_kernel(const float4 *__restrict__ pm, int n, PanelOrder order, fl
   int Ic, Jc;
   long long t;
   if (!panel_pair_of_block(order, blockIdx.x, Ic, Jc, t)) return;  // whole block: no barrier skipped
-  const int P = order.P;
+  Ic = __builtin_amdgcn_readfirstlane(Ic);
+  Jc = __builtin_amdgcn_readfirstlane(Jc);
   if (Ic == Jc)
-    sym_task<K, KP, W, IL, POT, ML, JL, true>(pm, n, Ic, Jc, P, eps2, part, csum, mis, jtile,
+    sym_task<K, KP, W, IL, POT, ML, JL, true>(pm, n, Ic, Jc, map, eps2, part, csum, mis, jtile,
                                               jsum);
   else
-    sym_task<K, KP, W, IL, POT, ML, JL, false>(pm, n, Ic, Jc, P, eps2, part, csum, mis, jtile,
+    sym_task<K, KP, W, IL, POT, ML, JL, false>(pm, n, Ic, Jc, map, eps2, part, csum, mis, jtile,
                                                jsum);
 }
 
-// a_i = G sum_J part[I][J][c][b] over J ascending; with POT the fourth sum is
-// phi_i and the output's w is Phi_i = -G phi_i, else w = 0.
+// The panel sums of one launch's slots (SlotMap map, columns [c0, c1)) added
+// into each touched body's sum in ascending J: a body of a panel K < c0
+// continues the fp32 running sum an earlier chunk left in out[i] and adds
+// its slots J = c0 .. c1 - 1; a body of a panel in [c0, c1) starts from 0
+// and adds J = 0 .. c1 - 1.  The last chunk (c1 = P) writes a_i = G * sum
+// (with POT the fourth sum is phi_i and w = Phi_i = -G phi_i, else w = 0);
+// earlier chunks write the unscaled running sums.  The bodies of panels
+// K >= c1 are not touched: the caller launches min(n, c1 B) threads.
 template <bool POT>
 __global__ __launch_bounds__(256) void symmetric_reduce_kernel(const float *__restrict__ part,
-                                                               int n, int P, int B, float G,
+                                                               int n, int B, SlotMap map,
+                                                               int last, float G,
                                                                float4 *__restrict__ out) {
   constexpr int NC = sym_sums<POT>();
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
-  const int I = i / B, b = i % B;
-  const float *s = part + (size_t)I * P * NC * B + b;
+  const int K = i / B, b = i % B;
   float sx = 0.0f, sy = 0.0f, sz = 0.0f, sp = 0.0f;
-  for (int J = 0; J < P; ++J, s += (size_t)NC * B) {
+  int J = 0;
+  if (K < map.c0) {
+    const float4 r = out[i];
+    sx = r.x;
+    sy = r.y;
+    sz = r.z;
+    sp = r.w;
+    J = map.c0;
+  }
+  const float *s = part + (size_t)map.slot(K, J) * NC * B + b;
+#pragma unroll 8
+  for (; J < map.c1; ++J, s += (size_t)NC * B) {
     sx += s[0];
     sy += s[B];
     sz += s[2 * B];
     if constexpr (POT) sp += s[3 * B];
   }
-  out[i] = make_float4(G * sx, G * sy, G * sz, POT ? -G * sp : 0.0f);
+  if (last)
+    out[i] = make_float4(G * sx, G * sy, G * sz, POT ? -G * sp : 0.0f);
+  else
+    out[i] = make_float4(sx, sy, sz, POT ? sp : 0.0f);
 }
 
 // (id, K, KP, waves, occupancy target, interleave width, i-masses in LDS,
@@ -473,10 +540,40 @@ size_t symmetric_workspace_bytes(int64_t n, int v, bool pot) {
   return (size_t)P * (size_t)P * (pot ? 4 : 3) * (size_t)B * sizeof(float);
 }
 
-hipError_t launch_symmetric_tasks(const float *posmass, int n, float eps2, int v, bool pot,
-                                  void *workspace, hipStream_t stream) {
+bool symmetric_chunk_ok(int chunk_panels) {
+  return chunk_panels > 0 && chunk_panels % kPanelTile == 0;
+}
+
+// Bytes of one chunk's slots: the largest over the chunks (the last full one).
+static size_t chunk_slot_bytes(int64_t n, int v, bool pot, int chunk_panels) {
+  const int64_t B = symmetric_panel(v, pot), P = symmetric_panels(n, v, pot);
+  long long most = 0;
+  for (int64_t c0 = 0; c0 < P; c0 += chunk_panels) {
+    const SlotMap map{(int)c0, (int)std::min<int64_t>(P, c0 + chunk_panels)};
+    most = std::max(most, map.slots());
+  }
+  // rounded up to 256 bytes, so that the second buffer starts aligned
+  const size_t bytes = (size_t)most * (pot ? 4 : 3) * (size_t)B * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+size_t symmetric_chunked_workspace_bytes(int64_t n, int v, bool pot, int chunk_panels) {
+  if (n <= 0 || v < 0 || v >= symmetric_variant_count(pot) || !symmetric_chunk_ok(chunk_panels))
+    return 0;
+  const int64_t P = symmetric_panels(n, v, pot);
+  // two buffers when there are two chunks or more (consecutive chunks run
+  // at the same time on two queues)
+  return chunk_slot_bytes(n, v, pot, chunk_panels) * (P > chunk_panels ? 2 : 1);
+}
+
+// The task kernel over the panel pairs with J in [c0, c1) (c0 a multiple of
+// the tile side; [0, P) for the whole pass), writing the slots of that chunk.
+static hipError_t launch_tasks_columns(const float *posmass, int n, float eps2, int v, bool pot,
+                                       void *workspace, int c0, int c1, hipStream_t stream) {
   const int P = (int)symmetric_panels(n, v, pot);
-  const PanelOrder order = panel_order(P);
+  const PanelOrder order =
+      panel_order_range(P, first_pair_of_column(c0), first_pair_of_column(c1));
+  const SlotMap map{c0, c1};
   const long long blocks = kXcds * order.per_xcd;
   float *part = reinterpret_cast<float *>(workspace);
   const float4 *pm = reinterpret_cast<const float4 *>(posmass);
@@ -485,8 +582,8 @@ hipError_t launch_symmetric_tasks(const float *posmass, int n, float eps2, int v
 #define X(id, K, KP, W, OCC, IL, ML, JL)                                               \
   case id:                                                                             \
     hipLaunchKernelGGL((symmetric_task_kernel<K, KP, W, OCC, IL, false, ML, JL>),      \
-                       dim3((unsigned)blocks), dim3(W * kWave), 0, stream, pm, n, order, eps2, \
-                       part);                                                          \
+                       dim3((unsigned)blocks), dim3(W * kWave), 0, stream, pm, n, order, map, \
+                       eps2, part);                                                    \
     break;
       NBODY_SYM_VARIANTS(X)
 #undef X
@@ -498,8 +595,8 @@ hipError_t launch_symmetric_tasks(const float *posmass, int n, float eps2, int v
 #define X(id, K, KP, W, OCC, ML, JL)                                                   \
   case id:                                                                             \
     hipLaunchKernelGGL((symmetric_task_kernel<K, KP, W, OCC, 1, true, ML, JL>),        \
-                       dim3((unsigned)blocks), dim3(W * kWave), 0, stream, pm, n, order, eps2, \
-                       part);                                                          \
+                       dim3((unsigned)blocks), dim3(W * kWave), 0, stream, pm, n, order, map, \
+                       eps2, part);                                                    \
     break;
       NBODY_SYM_POT_VARIANTS(X)
 #undef X
@@ -510,18 +607,37 @@ hipError_t launch_symmetric_tasks(const float *posmass, int n, float eps2, int v
   return hipGetLastError();
 }
 
-hipError_t launch_symmetric_reduce(int n, float G, float *accel, int v, bool pot,
-                                   const void *workspace, hipStream_t stream) {
+// The reduce of the chunk [c0, c1): the bodies of panels below c1.
+static hipError_t launch_reduce_columns(int n, float G, float *accel, int v, bool pot,
+                                        const void *workspace, int c0, int c1,
+                                        hipStream_t stream) {
   const int B = symmetric_panel(v, pot);
   const int P = (int)symmetric_panels(n, v, pot);
+  const int touched = (int)std::min<int64_t>(n, (int64_t)c1 * B);
+  const SlotMap map{c0, c1};
+  const int last = c1 == P;
   const float *part = reinterpret_cast<const float *>(workspace);
+  float4 *out = reinterpret_cast<float4 *>(accel);
+  const dim3 grid((touched + 255) / 256);
   if (pot)
-    hipLaunchKernelGGL(symmetric_reduce_kernel<true>, dim3((n + 255) / 256), dim3(256), 0, stream,
-                       part, n, P, B, G, reinterpret_cast<float4 *>(accel));
+    hipLaunchKernelGGL(symmetric_reduce_kernel<true>, grid, dim3(256), 0, stream, part, touched,
+                       B, map, last, G, out);
   else
-    hipLaunchKernelGGL(symmetric_reduce_kernel<false>, dim3((n + 255) / 256), dim3(256), 0,
-                       stream, part, n, P, B, G, reinterpret_cast<float4 *>(accel));
+    hipLaunchKernelGGL(symmetric_reduce_kernel<false>, grid, dim3(256), 0, stream, part, touched,
+                       B, map, last, G, out);
   return hipGetLastError();
+}
+
+hipError_t launch_symmetric_tasks(const float *posmass, int n, float eps2, int v, bool pot,
+                                  void *workspace, hipStream_t stream) {
+  return launch_tasks_columns(posmass, n, eps2, v, pot, workspace, 0,
+                              (int)symmetric_panels(n, v, pot), stream);
+}
+
+hipError_t launch_symmetric_reduce(int n, float G, float *accel, int v, bool pot,
+                                   const void *workspace, hipStream_t stream) {
+  return launch_reduce_columns(n, G, accel, v, pot, workspace, 0,
+                               (int)symmetric_panels(n, v, pot), stream);
 }
 
 hipError_t launch_symmetric(const float *posmass, int n, float G, float eps2, float *accel,
@@ -529,6 +645,87 @@ hipError_t launch_symmetric(const float *posmass, int n, float G, float eps2, fl
   const hipError_t e = launch_symmetric_tasks(posmass, n, eps2, v, pot, workspace, stream);
   if (e != hipSuccess) return e;
   return launch_symmetric_reduce(n, G, accel, v, pot, workspace, stream);
+}
+
+// The library's second queue on each GPU for the chunked pass: a side stream
+// (default priority) and a pool of events, made on first use with that GPU
+// current and kept until the process ends.  The mutex also keeps the
+// enqueue sequence of one chunked call from interleaving with another's.
+namespace {
+
+constexpr int kMaxSideDevices = 64;
+
+struct SideQueue {
+  hipStream_t stream = nullptr;
+  std::vector<hipEvent_t> events;
+};
+
+std::mutex g_side_mutex;
+SideQueue g_side[kMaxSideDevices];
+
+// Under g_side_mutex: the current GPU's side queue with at least `events`
+// events.
+hipError_t side_queue(int events, SideQueue *&q) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxSideDevices) return hipErrorInvalidDevice;
+  q = &g_side[dev];
+  if (!q->stream) {
+    e = hipStreamCreateWithFlags(&q->stream, hipStreamNonBlocking);
+    if (e != hipSuccess) {
+      q->stream = nullptr;
+      return e;
+    }
+  }
+  while ((int)q->events.size() < events) {
+    hipEvent_t ev = nullptr;
+    e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+    q->events.push_back(ev);
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+// Chunk c = [c0, c0 + C) runs on the caller's stream for even c and on the
+// side queue for odd c, in slot buffer c % 2: its panel-pair kernel may run
+// alongside the previous chunk's, so the tail of one launch is filled by the
+// next instead of leaving CUs idle.  Its reduce waits for the previous
+// chunk's reduce (event c - 1), since both add into the same running sums;
+// the next chunk on the same queue, which reuses the buffer, follows the
+// reduce in stream order.  The caller's stream waits for the last event, and
+// every side-queue operation is ordered before it.
+hipError_t launch_symmetric_chunked(const float *posmass, int n, float G, float eps2,
+                                    float *accel, int v, bool pot, int chunk_panels,
+                                    void *workspace, hipStream_t stream) {
+  const int P = (int)symmetric_panels(n, v, pot);
+  const int chunks = (P + chunk_panels - 1) / chunk_panels;
+  if (chunks == 1) {
+    const hipError_t e = launch_tasks_columns(posmass, n, eps2, v, pot, workspace, 0, P, stream);
+    if (e != hipSuccess) return e;
+    return launch_reduce_columns(n, G, accel, v, pot, workspace, 0, P, stream);
+  }
+  const size_t half = chunk_slot_bytes(n, v, pot, chunk_panels);
+  std::lock_guard<std::mutex> lock(g_side_mutex);
+  SideQueue *q = nullptr;
+  hipError_t e = side_queue(chunks + 1, q);
+  if (e != hipSuccess) return e;
+  hipEvent_t fork = q->events[chunks];
+  e = hipEventRecord(fork, stream);
+  if (e == hipSuccess) e = hipStreamWaitEvent(q->stream, fork, 0);
+  for (int c = 0; c < chunks && e == hipSuccess; ++c) {
+    const int c0 = c * chunk_panels, c1 = std::min(P, c0 + chunk_panels);
+    const hipStream_t s = (c % 2 == 0) ? stream : q->stream;
+    void *buf = static_cast<char *>(workspace) + (c % 2) * half;
+    e = launch_tasks_columns(posmass, n, eps2, v, pot, buf, c0, c1, s);
+    if (e == hipSuccess && c > 0) e = hipStreamWaitEvent(s, q->events[c - 1], 0);
+    if (e == hipSuccess) e = launch_reduce_columns(n, G, accel, v, pot, buf, c0, c1, s);
+    if (e == hipSuccess) e = hipEventRecord(q->events[c], s);
+  }
+  if (e == hipSuccess) e = hipStreamWaitEvent(stream, q->events[chunks - 1], 0);
+  return e;
 }
 
 }  // namespace nbody

@@ -34,8 +34,11 @@
  *  - Results are bitwise reproducible for a given (n, entry point, variant):
  *    every sum has a fixed order and no atomics are used.  See
  *    NBODY_SUMMATION_ORDER below.
- *  - The library keeps no state; calls on different streams may overlap as
- *    long as they do not write memory another call reads.
+ *  - The library keeps no state beyond two per-GPU resources made on first
+ *    use and kept until the process ends: the side stream and events of
+ *    nbody_accel_symmetric_chunked, and the static scratch of
+ *    nbody_energy_static.  Calls on different streams may overlap as long
+ *    as they do not write memory another call reads.
  */
 #ifndef NBODY_H
 #define NBODY_H
@@ -94,7 +97,9 @@ int nbody_abi_version(void);
  *              (m_max / 3.4e38)^(2/3) (2e-26 for m = 1, 2e-30 for m = 1e-6).
  *              Below it the self term m_i eps^-3 * 0 is inf * 0 and every
  *              acceleration comes out NaN; this is not checked (the masses
- *              are device data).  The same holds for every force pass.
+ *              are device data).  The same holds for the split-j passes; the
+ *              pair-symmetric passes have a further, mass-independent limit
+ *              (see nbody_accel_symmetric).
  *   accel_out  [n] float4, written: (ax, ay, az, 0).  Must not overlap
  *              posmass (NBODY_ERR_ALIAS).
  * The library picks a variant from n (nbody_accel_variant_for_n). */
@@ -217,6 +222,12 @@ size_t nbody_accel_splitj_tree_workspace_bytes(int64_t n, int64_t j_chunk, int t
  *              (12 n^2 / panel bytes: about 6.4 GB at n = 2^20), 16-byte
  *              aligned, disjoint from posmass and accel_out; contents on
  *              return are unspecified.
+ * eps2 range: a pair in two different panels forms inv^3 = (|r|^2 +
+ * eps^2)^(-3/2) in fp32 before either mass multiplies it (one product serves
+ * both bodies), so besides nbody_accel's limit eps2 must stay above about
+ * 2.1e-26 whatever the masses: below it inv^3 overflows for coincident
+ * bodies in different panels, and both their rows come out NaN (inf * 0).
+ * Diagonal panel pairs use nbody_accel's mass-first form.  Not checked.
  * Other arguments as nbody_accel.  NBODY_ERR_INVALID_ARG also when the
  * panel pairs exceed 2^31 - 1 (n beyond ~1.3e8). */
 int nbody_accel_symmetric(const float *posmass, int64_t n, float G, float eps2,
@@ -231,6 +242,43 @@ int nbody_accel_symmetric_variant_count(void);
 int nbody_accel_symmetric_panel(int variant);
 /* The variant nbody_accel_symmetric uses for n when passed -1. */
 int nbody_accel_symmetric_variant_for_n(int64_t n);
+
+/* nbody_accel_symmetric in column chunks, with a workspace that grows as n,
+ * not n^2.  The panel pairs (I, J) are taken chunk by chunk, a chunk being
+ * the pairs with J in a range of chunk_panels panels (ascending ranges);
+ * after each chunk's panel-pair kernel, a reduce kernel adds that chunk's
+ * panel sums into each touched body's fp32 running sum (kept in accel_out
+ * between chunks) in ascending panel order, and the last chunk multiplies by
+ * G.  Each body's panel sums are therefore added in the same order as by
+ * nbody_accel_symmetric, and accel_out is bitwise equal to its result for
+ * the same variant, whatever chunk_panels.
+ * Consecutive chunks run on two queues, in two halves of the workspace:
+ * even chunks on `stream`, odd chunks on a side stream the library creates
+ * for the current GPU on first use (default priority, kept until the
+ * process ends, with a pool of events), so that one chunk's panel-pair
+ * kernel fills the CUs the previous one's tail leaves idle.  The calls are
+ * ordered by events: the call is asynchronous on `stream` like every entry
+ * point, and work queued on `stream` after it starts only when the whole
+ * pass is done.  Calls on one GPU share the side stream (they are correct
+ * but serialise there); the stream must belong to the current HIP device.
+ *   chunk_panels  a positive multiple of 32 (the panel-pair tile side), or 0
+ *                 for NBODY_SYMMETRIC_DEFAULT_CHUNK.
+ *   workspace     >= nbody_accel_symmetric_chunked_workspace_bytes(n,
+ *                 variant, chunk_panels) bytes: two chunks' panel sums,
+ *                 about 48 n chunk_panels bytes (1.6 GB at n = 2^20 with
+ *                 32, against 6.4 GB for nbody_accel_symmetric; 9 GB at
+ *                 6e6 bodies, where the whole pass would need 211 GB).
+ *                 16-byte aligned, disjoint from posmass and accel_out;
+ *                 contents on return are unspecified.
+ * Two launches per chunk; other arguments and errors as
+ * nbody_accel_symmetric (NBODY_ERR_INVALID_ARG for a bad chunk_panels). */
+#define NBODY_SYMMETRIC_DEFAULT_CHUNK 32
+int nbody_accel_symmetric_chunked(const float *posmass, int64_t n, float G, float eps2,
+                                  float *accel_out, int variant, int chunk_panels,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+/* Workspace bytes for (n, variant, chunk_panels); 0 for n == 0, an unknown
+ * variant or a bad chunk_panels. */
+size_t nbody_accel_symmetric_chunked_workspace_bytes(int64_t n, int variant, int chunk_panels);
 
 /* nbody_accel_symmetric in its two phases, for callers that schedule them
  * themselves (other work between them, or timing the panel-pair kernel on

@@ -3,7 +3,10 @@
 // the launch grid take every pair (I, J), I <= J < P, exactly once; the
 // blocks of one XCD (b % 8) take a contiguous stretch of pair numbers in
 // ascending order; and within one tile column the pairs are those with
-// J in [cS, cS + S).  Only host code runs (no GPU is needed).
+// J in [cS, cS + S).  For column chunks: a chunk's launch takes exactly its
+// columns' pairs, every slot of its SlotMap is written once, and the chunk
+// reduces add each panel's sums in ascending J over all chunks.  Only host
+// code runs (no GPU is needed).
 #include <cstdio>
 #include <vector>
 
@@ -52,6 +55,89 @@ int main() {
     }
     if (taken != o.pairs) {
       std::printf("P=%d: %lld pairs taken, %lld expected\n", P, taken, o.pairs);
+      ++bad;
+    }
+    if (bad) break;
+    // Column chunks of C panels (C a multiple of the tile side): the blocks of
+    // a chunk's launch take exactly the pairs with J in [c0, c1), each once;
+    // every slot of the chunk's SlotMap is written by exactly one task side
+    // and lies in [0, slots()); and the reduces, chunk after chunk, add each
+    // panel's sums for J = 0 .. P-1 once each, in ascending J.
+    for (int C : {32, 64, 96, 128}) {
+      std::vector<int> next_j(P, 0);  // the J each panel's running sum expects next
+      for (int c0 = 0; c0 < P; c0 += C) {
+        const int c1 = P < c0 + C ? P : c0 + C;
+        const PanelOrder oc =
+            panel_order_range(P, first_pair_of_column(c0), first_pair_of_column(c1));
+        const SlotMap map{c0, c1};
+        const long long nslots = map.slots();
+        std::vector<unsigned char> written((size_t)nslots, 0);
+        long long got = 0;
+        for (long long b = 0; b < kXcds * oc.per_xcd; ++b) {
+          int I, J;
+          long long t;
+          if (!panel_pair_of_block(oc, b, I, J, t)) continue;
+          ++got;
+          if (J < c0 || J >= c1 || I > J) {
+            std::printf("P=%d C=%d chunk %d: pair (%d, %d) outside the chunk\n", P, C, c0, I, J);
+            ++bad;
+            continue;
+          }
+          const long long sides[2] = {map.slot(I, J), I < J ? map.slot(J, I) : -1};
+          for (long long sl : sides) {
+            if (sl == -1) continue;
+            if (sl < 0 || sl >= nslots || written[(size_t)sl]++) {
+              std::printf("P=%d C=%d chunk %d: slot %lld of pair (%d, %d) bad or reused\n", P,
+                          C, c0, sl, I, J);
+              ++bad;
+            }
+          }
+        }
+        if (got != first_pair_of_column(c1) - first_pair_of_column(c0)) {
+          std::printf("P=%d C=%d chunk %d: %lld pairs taken\n", P, C, c0, got);
+          ++bad;
+        }
+        for (long long sl = 0; sl < nslots; ++sl)
+          if (!written[(size_t)sl]) {
+            std::printf("P=%d C=%d chunk %d: slot %lld never written\n", P, C, c0, sl);
+            ++bad;
+            break;
+          }
+        // the reduce: panels K < c0 add J in [c0, c1), panels in the chunk
+        // start afresh and add J in [0, c1); slots of consecutive J adjacent
+        for (int K = 0; K < c1; ++K) {
+          const int jfirst = K < c0 ? c0 : 0;
+          if (K >= c0 && next_j[K] != 0) {
+            std::printf("P=%d C=%d: panel %d starts again at chunk %d\n", P, C, K, c0);
+            ++bad;
+          }
+          if (K < c0 && next_j[K] != c0) {
+            std::printf("P=%d C=%d: panel %d expects J=%d at chunk %d\n", P, C, K, next_j[K],
+                        c0);
+            ++bad;
+          }
+          for (int J = jfirst; J < c1; ++J)
+            if (J > jfirst && map.slot(K, J) != map.slot(K, J - 1) + 1) {
+              std::printf("P=%d C=%d: panel %d slots not consecutive at J=%d\n", P, C, K, J);
+              ++bad;
+              break;
+            }
+          next_j[K] = c1;
+        }
+      }
+      for (int K = 0; K < P; ++K)
+        if (next_j[K] != P) {
+          std::printf("P=%d C=%d: panel %d summed up to J=%d only\n", P, C, K, next_j[K]);
+          ++bad;
+          break;
+        }
+      if (bad) break;
+    }
+    // the whole pass is the chunk [0, P): slot K P + J
+    const SlotMap whole{0, P};
+    if (P > 1 && (whole.slot(P - 1, 1) != (long long)(P - 1) * P + 1 ||
+                  whole.slots() != (long long)P * P)) {
+      std::printf("P=%d: whole-pass slots are not K P + J\n", P);
       ++bad;
     }
     if (bad) break;

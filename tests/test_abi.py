@@ -385,3 +385,33 @@ def test_energy_static_validation(lib):
     assert nb.nbody_energy_workspace_bytes(nmax + 1) > nb.NBODY_ENERGY_STATIC_SCRATCH_BYTES
     assert f(vp(A), vp(B), nmax + 1, 1.0, 1e-4, vp(C), None) == nb.NBODY_ERR_WORKSPACE
     assert f(vp(A), vp(B), 10 ** 7, 1.0, 1e-4, vp(C), None) == nb.NBODY_ERR_WORKSPACE
+
+
+def test_symmetric_chunked_sizes_and_validation(lib):
+    """Chunked workspace: one chunk's slots (the largest chunk is the last
+    full one), far below the whole pass's at 10^6 bodies; bad chunk widths and
+    short workspaces are rejected before anything is enqueued."""
+    n = 1 << 20
+    panel, P = 2048, 512
+    v = nb.nbody_accel_symmetric_variant_for_n(n)
+    assert nb.nbody_accel_symmetric_panel(v) == panel
+    # two buffers of the largest chunk: the last one, where panels 480..511
+    # take all J < 512 and panels 0..479 take 32 each
+    assert nb.nbody_accel_symmetric_chunked_workspace_bytes(n, v, 32) == (
+        2 * (480 * 32 + 32 * 512) * 3 * panel * 4)
+    assert nb.nbody_accel_symmetric_chunked_workspace_bytes(n, v, 0) == (
+        nb.nbody_accel_symmetric_chunked_workspace_bytes(n, v, 32))
+    # one chunk covering every panel: one buffer, the whole pass's slots
+    assert nb.nbody_accel_symmetric_chunked_workspace_bytes(n, v, P) == (
+        nb.nbody_accel_symmetric_workspace_bytes(n, v))
+    assert nb.nbody_accel_symmetric_chunked_workspace_bytes(n, v, 31) == 0
+    assert nb.nbody_accel_symmetric_chunked_workspace_bytes(n, v, -32) == 0
+    assert nb.nbody_accel_symmetric_chunked_workspace_bytes(0, v, 32) == 0
+    f = lib.nbody_accel_symmetric_chunked
+    need = nb.nbody_accel_symmetric_chunked_workspace_bytes(1000, -1, 32)
+    assert f(vp(A), 1000, 1.0, 1e-4, vp(B), -1, 48, vp(C), need, None) == nb.NBODY_ERR_INVALID_ARG
+    assert f(vp(A), 1000, 1.0, 1e-4, vp(B), -1, 32, vp(C), need - 1, None) == (
+        nb.NBODY_ERR_WORKSPACE)
+    assert f(vp(A), 1000, 1.0, 0.0, vp(B), -1, 32, vp(C), need, None) == nb.NBODY_ERR_INVALID_ARG
+    assert f(vp(A), 1000, 1.0, 1e-4, vp(A), -1, 32, vp(C), need, None) == nb.NBODY_ERR_ALIAS
+    assert f(vp(A), 0, 1.0, 1e-4, vp(B), -1, 32, None, 0, None) == nb.NBODY_OK

@@ -397,6 +397,89 @@ def test_symmetric_collision1m_ragged_sampled():
 
 
 # ---------------------------------------------------------------------------
+# Pair-symmetric pass in column chunks (bounded workspace)
+# ---------------------------------------------------------------------------
+
+def sym_chunked(pm_np, G=1.0, eps2=1e-4, variant=-1, chunk=0):
+    t = torch.from_numpy(pm_np).to(DEV)
+    out = torch.full_like(t, float("nan"))
+    n = pm_np.shape[0]
+    ws = torch.empty(max(nb.nbody_accel_symmetric_chunked_workspace_bytes(n, variant, chunk), 16),
+                     dtype=torch.uint8, device=DEV)
+    nb.nbody_accel_symmetric_chunked(t, G, eps2, out, ws, variant, chunk)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("n", [1, 3, 1000, 9000, 20000, 70001])
+def test_symmetric_chunked_bitwise_equals_whole_pass(n):
+    """Every variant, in chunks of 32, 64 and 96 panels: the same result as
+    the whole pass bit for bit (each body's panel sums are added in the same
+    ascending order, the running sum carried in accel_out between chunks).
+    9000 and 20000 bodies give 36 and 79 panels of 256 (two and three
+    chunks, the last ragged); 70001 gives 69 panels of 1024."""
+    pm, _ = workloads.uniform_cube(n, seed=500 + n % 89, masses="lognormal")
+    variants = (range(nb.nbody_accel_symmetric_variant_count()) if n <= 20000
+                else (-1, 15, 20))
+    for v in variants:
+        whole = sym_accel(pm, 0.5, 1e-4, v)
+        for chunk in (32, 64, 96):
+            log(f"chunked n={n} variant={v} chunk={chunk}")
+            assert np.array_equal(sym_chunked(pm, 0.5, 1e-4, v, chunk), whole), (n, v, chunk)
+
+
+@pytest.mark.parametrize("name", ["plummer1m", "collision1m"])
+def test_symmetric_chunked_large_workloads(name):
+    """The library's variant at 2^20 and at 1,000,003 bodies (512 and 489
+    panels of 2048: 16 chunks of 32, the last one ragged at 1,000,003), in
+    the default chunks: bitwise equal to the whole pass, in a workspace of
+    about 1.5 GB instead of 6.4 GB."""
+    w = workloads.WORKLOADS[name]
+    pm, _ = workloads.make(name)
+    need = nb.nbody_accel_symmetric_chunked_workspace_bytes(w.n)
+    whole_need = nb.nbody_accel_symmetric_workspace_bytes(w.n)
+    log(f"{name}: chunked workspace {need / 2**30:.2f} GiB, whole pass {whole_need / 2**30:.2f} GiB")
+    assert need * 3 < whole_need
+    a = sym_chunked(pm, w.G, w.eps2)
+    assert np.array_equal(a, sym_accel(pm, w.G, w.eps2))
+
+
+def test_symmetric_chunked_is_stream_ordered():
+    """The chunked pass runs its odd chunks on the library's side stream and
+    joins it back with events: work queued after it on the caller's stream
+    sees the finished result.  Three calls back to back without a
+    synchronisation (the event pool re-recorded while earlier waits are still
+    queued), a call on a torch side stream followed by a kick on that stream,
+    and two calls on two streams at once all match the whole pass bitwise."""
+    n = 40000                                   # 40 panels of 1024: chunks of 32 and 8
+    pms = [workloads.uniform_cube(n, seed=700 + k, masses="lognormal")[0] for k in range(3)]
+    ref = [sym_accel(p) for p in pms]
+    ts = [torch.from_numpy(p).to(DEV) for p in pms]
+    need = nb.nbody_accel_symmetric_chunked_workspace_bytes(n)
+    wss = [torch.empty(need, dtype=torch.uint8, device=DEV) for _ in range(3)]
+    outs = [torch.full_like(ts[0], float("nan")) for _ in range(3)]
+    torch.cuda.synchronize()
+    for k in range(3):
+        nb.nbody_accel_symmetric_chunked(ts[k], 1.0, 1e-4, outs[k], wss[k])
+    copies = [o.clone() for o in outs]          # queued after the calls, no sync
+    torch.cuda.synchronize()
+    for k in range(3):
+        assert np.array_equal(copies[k].cpu().numpy(), ref[k]), k
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()    # default priority
+    vel = torch.zeros_like(ts[0])
+    out_a, out_b = torch.full_like(ts[0], float("nan")), torch.full_like(ts[0], float("nan"))
+    torch.cuda.synchronize()
+    nb.nbody_accel_symmetric_chunked(ts[0], 1.0, 1e-4, out_a, wss[0], stream=s1)
+    nb.nbody_kick(vel, out_a, 1.0, stream=s1)   # v = 0 + 1 * a
+    nb.nbody_accel_symmetric_chunked(ts[1], 1.0, 1e-4, out_b, wss[1], stream=s2)
+    s1.synchronize()
+    s2.synchronize()
+    assert np.array_equal(out_a.cpu().numpy(), ref[0])
+    assert np.array_equal(out_b.cpu().numpy(), ref[1])
+    assert np.array_equal(vel.cpu().numpy()[:, :3], ref[0][:, :3])
+
+
+# ---------------------------------------------------------------------------
 # One GPU's share of the i side
 # ---------------------------------------------------------------------------
 
@@ -540,6 +623,32 @@ def test_tiny_softening_fp32_range(path):
     rows = sample_rows(n, 128, seed=10)
     assert_parity(a[rows], ref_accel(pm, 1.0, 1e-24, rows), f"eps2 1e-24 {path}")
     assert np.all(np.isnan(PATHS[path](pm, 1.0, 1e-27)[:, :3]))
+
+
+@pytest.mark.parametrize("path", sorted(PATHS))
+def test_tiny_softening_small_masses(path):
+    """eps2 = 1e-28 with masses 1e-6 and two coincident bodies (10 and 2500,
+    in different panels of every pair-symmetric variant): the mass-first pair
+    form of the one-sided and split-j passes keeps m eps^-3 = 1e36 finite, so
+    every row matches the oracle; the pair-symmetric passes form inv^3 =
+    1e42 before the mass, which overflows, so exactly the two coincident
+    bodies' rows are NaN and every other row matches the oracle (the limit
+    documented for nbody_accel_symmetric)."""
+    n = 3000
+    pm, _ = workloads.uniform_cube(n, seed=64)
+    pm[:, 3] = 1e-6
+    pm[2500, :3] = pm[10, :3]
+    a = PATHS[path](pm, 1.0, 1e-28)
+    ref = ref_accel(pm, 1.0, 1e-28)
+    if path.startswith("symmetric"):
+        bad = [10, 2500]
+        assert np.all(np.isnan(a[bad, :3]))
+        rest = np.setdiff1d(np.arange(n), bad)
+        assert np.all(np.isfinite(a[rest]))
+        assert_parity(a[rest], ref[rest], f"eps2 1e-28 m 1e-6 {path}")
+    else:
+        assert np.all(np.isfinite(a))
+        assert_parity(a, ref, f"eps2 1e-28 m 1e-6 {path}")
 
 
 @pytest.mark.parametrize("path", sorted(PATHS))
