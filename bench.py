@@ -349,6 +349,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-one-sided", action="store_true",
                     help="skip timing the one-sided pass beside the pair-symmetric one")
+    ap.add_argument("--no-chunked", action="store_true",
+                    help="skip timing the chunked pair-symmetric pass beside the whole one")
     ap.add_argument("--sweep", action="store_true",
                     help="time the force pass of every compiled variant (one JSON line each) "
                          "instead of the step benchmark")
@@ -495,6 +497,16 @@ def main():
         one_ms, _ = nb.nbody_time_accel(pm, w.G, w.eps2, acc, nb.NBODY_PASS_ONE_SIDED, 2)
         log(f"one-sided nbody_accel: {min(one_ms):.3f} ms")
 
+    # the same pass in column chunks (bounded workspace, bitwise equal)
+    chunked_ms = chunked_ws = None
+    if args.path == "symmetric" and not args.no_chunked:
+        chunked_ws = nb.nbody_accel_symmetric_chunked_workspace_bytes(w.n, variant)
+        cws = torch.empty(chunked_ws, dtype=torch.uint8, device=dev)
+        chunked_ms = min(_time(nb, lambda: nb.nbody_accel_symmetric_chunked(
+            pm, w.G, w.eps2, acc, cws, variant), 2))
+        del cws
+        log(f"chunked pass: {chunked_ms:.3f} ms in {chunked_ws / 2**30:.2f} GiB")
+
     # energy diagnostic (outside the timed steps)
     ws = torch.empty(nb.nbody_energy_workspace_bytes(w.n), dtype=torch.uint8, device=dev)
     stats = torch.zeros(8, dtype=torch.float64, device=dev)
@@ -553,6 +565,8 @@ def main():
         "pairs_evaluated_per_interaction": 1.0 if args.path == "tile" else 0.5,
         "fp32_flops_issued_per_interaction": issued,
         "fp32_issued_frac": issued * inter / (kernel_avg * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
+        "chunked_force_ms": chunked_ms,
+        "chunked_workspace_bytes": chunked_ws,
         "one_sided_force_ms": min(one_ms) if one_ms else None,
         "one_sided_frac": (FLOPS_PER_INTERACTION * inter / (min(one_ms) * 1e-3) / 1e12
                            / PEAK_FP32_TFLOPS) if one_ms else None,

@@ -88,6 +88,11 @@ def cmd_run(args):
         ws = torch.empty(nb.nbody_accel_symmetric_workspace_bytes(w.n, v), dtype=torch.uint8,
                          device=dev)
         nb.nbody_accel_symmetric(pm, w.G, w.eps2, acc, ws, v)
+    elif args.path == "symmetric_chunked":
+        v = args.variant if args.variant is not None else nb.nbody_accel_symmetric_variant_for_n(w.n)
+        ws = torch.empty(nb.nbody_accel_symmetric_chunked_workspace_bytes(w.n, v),
+                         dtype=torch.uint8, device=dev)
+        nb.nbody_accel_symmetric_chunked(pm, w.G, w.eps2, acc, ws, v)
     else:
         v = args.variant if args.variant is not None else nb.nbody_accel_variant_for_n(w.n)
         nb.nbody_accel_variant(pm, w.G, w.eps2, acc, v)
@@ -277,7 +282,8 @@ def main():
     r = sub.add_parser("run")
     r.add_argument("--workload", default="plummer1m")
     r.add_argument("--variant", type=int, default=None)
-    r.add_argument("--path", choices=("tile", "symmetric", "energy"), default="symmetric")
+    r.add_argument("--path", choices=("tile", "symmetric", "symmetric_chunked", "energy"),
+                   default="symmetric")
     q = sub.add_parser("sq-report", help="SQ/GRBM counters of one kernel, with derived rates")
     q.add_argument("--dir", required=True)
     q.add_argument("--kernel", required=True, help="a substring of the kernel name")
