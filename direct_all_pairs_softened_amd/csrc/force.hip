@@ -292,37 +292,30 @@ static hipError_t launch_tile(const L &lay, int n, int i0, int ni, float G, floa
 }
 
 // (id, K, T, waves, S, unroll, occupancy target).  Ids are part of the ABI
-// (nbody_accel_variant).  Waves per SIMD at n = 2^20 are noted for the
-// large-n rows (1024 SIMDs; at most 8 waves resident per SIMD).
+// (nbody_accel_variant):
+//  0  the library's choice up to 2e5 bodies: 64 i-bodies per block, j split
+//     16 ways over 16 waves;
+//  1  the choice above: 2 i-bodies per lane, 8-wave blocks in 2 j parts, a
+//     register budget that fits 8 waves per SIMD (1024 blocks at 2^20);
+//  2-4  variant 1 with the inner j loop unrolled 1, 2 and 8 times instead of
+//     4: the unroll sweep (the tunable of the CUDA Handbook's Table 14-2);
+//  5  2 i-bodies per lane in 4-wave blocks without a j split: the LDS twin of
+//     the LDS-free variants 6 and 7 (same K, T and j order, so bitwise equal).
+// Earlier tilings (1 to 8 i-bodies per lane, tiles of 64 to 512, 4 to 16
+// waves, j splits of 1 to 16) were measured on MI355X and are not kept.
 #define NBODY_FORCE_VARIANTS(X)  \
-  X(0, 1, 256, 4, 1, 4, 0)       /* 4096 blocks, 16 waves/SIMD (two rounds) */ \
-  X(1, 2, 256, 4, 1, 4, 0)       /* 2048 blocks, 8 waves/SIMD */               \
-  X(2, 4, 256, 4, 1, 4, 0)       /* 1024 blocks, 4 waves/SIMD */               \
-  X(3, 8, 256, 4, 1, 2, 0)       /* 512 blocks, 2 waves/SIMD */                \
-  X(4, 4, 512, 4, 1, 4, 0)                                                     \
-  X(5, 2, 512, 4, 1, 4, 0)                                                     \
-  X(6, 4, 256, 4, 1, 1, 0)                                                     \
-  X(7, 4, 256, 4, 1, 8, 0)                                                     \
-  X(8, 1, 256, 8, 2, 4, 0)                                                     \
-  X(9, 2, 256, 8, 2, 4, 0)                                                     \
-  X(10, 1, 256, 16, 4, 4, 0)                                                   \
-  X(11, 1, 64, 16, 16, 4, 0)     /* small n: 64 i per block */                 \
-  X(12, 2, 128, 16, 8, 4, 0)     /* small n: 128 i per block */                \
-  X(13, 4, 256, 8, 2, 1, 8)      /* 1024 blocks x 8 waves: 8 waves/SIMD */     \
-  X(14, 4, 256, 8, 2, 2, 8)                                                    \
-  X(15, 2, 256, 4, 1, 4, 8)                                                    \
-  X(16, 2, 256, 8, 2, 4, 8)      /* 1024 blocks x 8 waves */                   \
-  X(17, 8, 256, 16, 4, 2, 4)     /* 512 blocks x 16 waves, 4+ waves/SIMD */    \
-  X(18, 4, 512, 8, 2, 2, 8)                                                    \
-  X(19, 2, 512, 8, 1, 4, 8)      /* 1024 i per block, 1024 blocks x 8 waves */
+  X(0, 1, 64, 16, 16, 4, 0)      \
+  X(1, 2, 256, 8, 2, 4, 8)       \
+  X(2, 2, 256, 8, 2, 1, 8)       \
+  X(3, 2, 256, 8, 2, 2, 8)       \
+  X(4, 2, 256, 8, 2, 8, 8)       \
+  X(5, 2, 256, 4, 1, 4, 0)
 
 // LDS-free variants: (id, K, T, waves, mode, occupancy target); mode 0 =
 // scalar loads of j, 1 = vector loads of one address per wave.
 #define NBODY_STREAM_VARIANTS(X) \
-  X(20, 2, 256, 4, 0, 0)         \
-  X(21, 4, 256, 4, 0, 0)         \
-  X(22, 2, 256, 4, 1, 0)         \
-  X(23, 4, 256, 4, 1, 0)
+  X(6, 2, 256, 4, 0, 0)          \
+  X(7, 2, 256, 4, 1, 0)
 
 static const ForceVariant kVariants[] = {
 #define X(id, K, T, W, S, U, OCC) {K, T, W, S, U, 0},
@@ -345,8 +338,8 @@ const ForceVariant *force_variant(int v) {
 // lane in 8-wave blocks (two j parts) with a VGPR budget that fits 8 waves
 // per SIMD is fastest.
 int force_variant_for_n(int64_t n) {
-  if (n <= 200000) return 11;  // 64 i per block, j split 16 ways
-  return 16;                   // 512 i per block, j split 2 ways, 8 waves/SIMD
+  if (n <= 200000) return 0;  // 64 i per block, j split 16 ways
+  return 1;                   // 512 i per block, j split 2 ways, 8 waves/SIMD
 }
 
 template <class L>
@@ -366,8 +359,8 @@ static hipError_t dispatch(int v, const L &lay, int n, int i0, int ni, float G, 
 // Variants compiled with the potential sum (the ones force_variant_for_n
 // picks).
 #define NBODY_POT_VARIANTS(X) \
-  X(11, 1, 64, 16, 16, 4, 0)  \
-  X(16, 2, 256, 8, 2, 4, 8)
+  X(0, 1, 64, 16, 16, 4, 0)   \
+  X(1, 2, 256, 8, 2, 4, 8)
 
 hipError_t launch_force_potential(const float *posmass, int n, float G, float eps2,
                                   float *accel, hipStream_t stream) {

@@ -426,63 +426,47 @@ __global__ __launch_bounds__(256) void symmetric_reduce_kernel(const float *__re
 
 // (id, K, KP, waves, occupancy target, interleave width, i-masses in LDS,
 // JL: 0 = rotated j-state, else LDS-carried with JL steps per unrolled
-// block); panel B = 64 * waves * K.  Interleave widths 2 and 4 (variants 12,
-// 13) measured the same as 1 on MI355X: under the 6-waves-per-SIMD register
-// budget the compiler schedules the pairs one after the other either way.
-// Variant 14 keeps 5 of its 8 i-masses in LDS (read once per pair inside the
-// step), which lets K = 8 fit 72 VGPRs without spilling: 7 waves per SIMD
-// instead of 6, and 193 against 206 ms at 2^20 bodies.  Asking for 8 waves
-// instead (64 VGPRs) makes the compiler spill to scratch inside the step
-// loop: 197 ms, and ~9 GB more memory traffic per pass.  Variant 15 is 14
-// with the j-state carried in LDS (7 waves; a few spills outside the step
-// loop): 181 against 195 ms for variant 14 on the same box; 16 (i-masses in
-// registers, 6 waves) and 18 (six i-masses in LDS) measured 1-3 % slower.
-// Variant 17 is its 1024-body-panel form.  With the j-state in LDS the
-// per-pair cost of a small K is low, so K = 4 (20: 64 VGPRs, 8 waves per
-// SIMD, no spills) and K = 2 (19) serve the smaller sizes.
+// block); panel B = 64 * waves * K.  Ids are part of the ABI
+// (nbody_accel_symmetric):
+//  0  8 i-bodies per lane in 4-wave blocks (2048-body panels), five of the
+//     eight i-masses in LDS so that the kernel fits 72 VGPRs (7 waves per
+//     SIMD): the library's choice above 3e5 bodies;
+//  1  4 i-bodies per lane in 4-wave blocks (1024-body panels, 8 waves per
+//     SIMD): from 77824 to 3e5 bodies;
+//  2  4 i-bodies per lane in one-wave blocks (256-body panels): from 30720
+//     to 77824 bodies;
+//  3  2 i-bodies per lane in one-wave blocks (128-body panels): up to 30720
+//     bodies, where larger panels leave too few panel pairs to fill the
+//     chip's 8192 wave slots;
+//  4  variant 0 with the j-state rotated one lane per step by DPP instead of
+//     carried in LDS (7 / K moves per pair): the ablation of the LDS
+//     carriage (the same panel shape; the j-side sums are added in another
+//     order, so it agrees with 0 to rounding).
+// One-wave blocks need no barrier: the wave adds its own j-side sums.
+// Other shapes measured on MI355X and not kept: the rotated carriage with 2
+// j-bodies per lane, 4 to 16 i-bodies per lane, 6 to 8 waves per SIMD, pair
+// interleave widths 2 and 4 (the same as 1 under this register budget), 6 or
+// all 8 i-masses in LDS, and 2 i-bodies per lane in 2-wave blocks.
 #define NBODY_SYM_VARIANTS(X) \
-  X(0, 8, 2, 4, 4, 1, 0, 0)     \
-  X(1, 8, 1, 4, 4, 1, 0, 0)     \
-  X(2, 4, 2, 4, 6, 1, 0, 0)     \
-  X(3, 8, 2, 8, 4, 1, 0, 0)     \
-  X(4, 4, 4, 4, 4, 1, 0, 0)     \
-  X(5, 8, 1, 8, 4, 1, 0, 0)     \
-  X(6, 16, 1, 4, 2, 1, 0, 0)    \
-  X(7, 12, 1, 4, 3, 1, 0, 0)    \
-  X(8, 8, 1, 2, 4, 1, 0, 0)     \
-  X(9, 8, 1, 4, 6, 1, 0, 0)     \
-  X(10, 6, 1, 4, 5, 1, 0, 0)    \
-  X(11, 16, 1, 2, 2, 1, 0, 0)   \
-  X(12, 8, 1, 4, 6, 4, 0, 0)    \
-  X(13, 8, 1, 4, 6, 2, 0, 0)    \
-  X(14, 8, 1, 4, 7, 1, 5, 0)    \
-  X(15, 8, 1, 4, 7, 1, 5, 8)    \
-  X(16, 8, 1, 4, 6, 1, 0, 8)    \
-  X(17, 8, 1, 2, 7, 1, 5, 8)    \
-  X(18, 8, 1, 4, 7, 1, 6, 8)    \
-  X(19, 2, 1, 2, 8, 1, 0, 8)    \
-  X(20, 4, 1, 4, 8, 1, 0, 8)
+  X(0, 8, 1, 4, 7, 1, 5, 8)     \
+  X(1, 4, 1, 4, 8, 1, 0, 8)     \
+  X(2, 4, 1, 1, 8, 1, 0, 8)     \
+  X(3, 2, 1, 1, 8, 1, 0, 8)     \
+  X(4, 8, 1, 4, 7, 1, 5, 0)
 
 // Variants of the pass that also sums the potential (id, K, KP, waves,
 // occupancy target, i-masses in LDS, JL as above); the ids are their own
-// (nbody_accel_symmetric_potential).  The potential sums take K = 8 to ~96
-// VGPRs (5 waves per SIMD, variant 3: 266 ms at 2^20 bodies); capping it at
-// 80 (6 waves) leaves a few spills outside the step loop and, with 2 of the
-// i-masses in LDS, takes 216 ms (variant 1).  With the j-state in LDS,
-// 5 waves and 4 i-masses in LDS (variant 6, no spills) it takes 203 ms.
-// Variants 7, 8 and 9 are 1024-body (K = 8 and K = 4) and 256-body panel
-// forms; 8 and 9 share the shapes of the plain variants 20 and 19.
+// (nbody_accel_symmetric_potential), and variant v has the panel shape and
+// j-state carriage of the plain variant v, so their xyz outputs are bitwise
+// equal.  The potential sums cost registers: with 8 i-bodies per lane,
+// 4 i-masses in LDS and 5 waves per SIMD (no spills); rotated instead, K = 8
+// took ~96 VGPRs (266 ms at 2^20 bodies) or 80 with spills (216 ms), against
+// 201 ms for variant 0.
 #define NBODY_SYM_POT_VARIANTS(X) \
-  X(0, 8, 1, 2, 6, 0, 0)          \
-  X(1, 8, 1, 4, 6, 2, 0)          \
-  X(2, 6, 1, 4, 6, 0, 0)          \
-  X(3, 8, 1, 4, 5, 0, 0)          \
-  X(4, 8, 1, 4, 6, 6, 8)          \
-  X(5, 8, 1, 4, 5, 8, 8)          \
-  X(6, 8, 1, 4, 5, 4, 8)          \
-  X(7, 8, 1, 2, 5, 4, 8)          \
-  X(8, 4, 1, 4, 8, 0, 8)          \
-  X(9, 2, 1, 2, 8, 0, 8)
+  X(0, 8, 1, 4, 5, 4, 8)          \
+  X(1, 4, 1, 4, 8, 0, 8)          \
+  X(2, 4, 1, 1, 8, 0, 8)          \
+  X(3, 2, 1, 1, 8, 0, 8)
 
 struct SymVariant {
   int K, KP, W;
@@ -508,20 +492,20 @@ int symmetric_variant_count(bool pot) {
   return pot ? (int)(sizeof(kSymPot) / sizeof(kSymPot[0])) : (int)(sizeof(kSym) / sizeof(kSym[0]));
 }
 
-// Measured on MI355X (force-pass sweeps), all with the j-state in LDS: 8
-// i-bodies per lane in 2048-body panels at 7 waves per SIMD (15) from ~2.5e5
-// bodies on (45.6 ms at 2^19 bodies, against 47.5 ms for 20); 4 i-bodies per
-// lane in 1024-body panels at 8 waves (20) from ~3e4 to ~2.5e5 (0.89 ms at
-// 65536 bodies, 3.17 ms at 131072, against 1.10 and 3.37 ms for 17); 2
-// i-bodies per lane in 256-body panels (19) below that, where larger panels
-// leave too few panel pairs to fill the chip (0.107 ms at 16384 bodies,
-// against 0.30 ms for the rotated 8; the one-sided nbody_accel takes 0.10
-// ms there).  The potential variants follow the same split by n, with the
-// same panel shapes and j-state carriage, so their xyz equal the plain
-// pass's.
+// Measured on MI355X (force-pass sweeps of every variant on Plummer spheres
+// of 8192 to 524288 bodies), all with the j-state in LDS: 2 i-bodies per
+// lane in one-wave blocks up to ~30000 bodies (86.8 us at 16384 against
+// 102.0 us for 4 i-bodies and 100.4 us for the one-sided pass; 193.7 against
+// 200.4 us at 28672, 255.4 against 245.6 us at 32768), 4 in one-wave blocks
+// up to ~78000 (1.035 against 1.053 ms at 73728, 1.288 against 1.236 ms at
+// 81920), 4 in 4-wave blocks up to ~3e5 (12.07 against 12.29 ms at 262144,
+// the same at 327680), 8 in 4-wave blocks above (26.7 against 27.0 ms at
+// 393216, 46.9 against 47.8 ms at 2^19).  The potential variants follow the
+// same split, with the same panel shapes and j-state carriage, so their xyz
+// equal the plain pass's.
 int symmetric_variant_for_n(int64_t n, bool pot) {
-  if (pot) return n <= 32768 ? 9 : n <= 200000 ? 8 : 6;
-  return n <= 32768 ? 19 : n <= 200000 ? 20 : 15;
+  (void)pot;
+  return n <= 30720 ? 3 : n <= 77824 ? 2 : n <= 300000 ? 1 : 0;
 }
 
 int symmetric_panel(int v, bool pot) {
