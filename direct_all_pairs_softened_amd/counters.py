@@ -87,15 +87,18 @@ def cmd_run(args):
         v = args.variant if args.variant is not None else nb.nbody_accel_symmetric_variant_for_n(w.n)
         ws = torch.empty(nb.nbody_accel_symmetric_workspace_bytes(w.n, v), dtype=torch.uint8,
                          device=dev)
-        nb.nbody_accel_symmetric(pm, w.G, w.eps2, acc, ws, v)
+        for _ in range(args.reps):
+            nb.nbody_accel_symmetric(pm, w.G, w.eps2, acc, ws, v)
     elif args.path == "symmetric_chunked":
         v = args.variant if args.variant is not None else nb.nbody_accel_symmetric_variant_for_n(w.n)
         ws = torch.empty(nb.nbody_accel_symmetric_chunked_workspace_bytes(w.n, v),
                          dtype=torch.uint8, device=dev)
-        nb.nbody_accel_symmetric_chunked(pm, w.G, w.eps2, acc, ws, v)
+        for _ in range(args.reps):
+            nb.nbody_accel_symmetric_chunked(pm, w.G, w.eps2, acc, ws, v)
     else:
         v = args.variant if args.variant is not None else nb.nbody_accel_variant_for_n(w.n)
-        nb.nbody_accel_variant(pm, w.G, w.eps2, acc, v)
+        for _ in range(args.reps):
+            nb.nbody_accel_variant(pm, w.G, w.eps2, acc, v)
     torch.cuda.synchronize()
     print(f"counters run: copy {COPY_BYTES} B, {args.path} force variant {v} on {w.name}",
           flush=True)
@@ -125,6 +128,9 @@ def cmd_sq_report(args):
                   f"{100 * v['SQ_ACTIVE_INST_VALU2'] / (g * 256):.1f} %")
         if "SQ_BUSY_CU_CYCLES" in v:
             print(f"- SIMD quad-cycles busy: {100 * v['SQ_BUSY_CU_CYCLES'] / (g * 256):.1f} %")
+        if "SQ_WAVE_CYCLES" in v:
+            # SQ_WAVE_CYCLES adds the resident waves every fourth cycle
+            print(f"- mean resident waves per SIMD: {4 * v['SQ_WAVE_CYCLES'] / g / 1024:.2f}")
 
 
 def read_counters(pattern):
@@ -282,6 +288,7 @@ def main():
     r = sub.add_parser("run")
     r.add_argument("--workload", default="plummer1m")
     r.add_argument("--variant", type=int, default=None)
+    r.add_argument("--reps", type=int, default=1, help="force passes, back to back")
     r.add_argument("--path", choices=("tile", "symmetric", "symmetric_chunked", "energy"),
                    default="symmetric")
     q = sub.add_parser("sq-report", help="SQ/GRBM counters of one kernel, with derived rates")

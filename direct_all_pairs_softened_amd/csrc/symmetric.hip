@@ -129,6 +129,20 @@ __device__ __forceinline__ int fresh_lane() {
   return l;
 }
 
+// A wave's issue priority from how far it has come: 3 in the first quarter
+// of its steps, down to 0 in the last (quarter is wave-uniform).  The SIMD
+// issues from the highest priority first, so waves that are behind catch up.
+__device__ __forceinline__ void pace(int quarter) {
+  if (quarter <= 0)
+    __builtin_amdgcn_s_setprio(3);
+  else if (quarter == 1)
+    __builtin_amdgcn_s_setprio(2);
+  else if (quarter == 2)
+    __builtin_amdgcn_s_setprio(1);
+  else
+    __builtin_amdgcn_s_setprio(0);
+}
+
 // Sums kept per body: the three acceleration components, plus the potential
 // sum with POT.
 template <bool POT>
@@ -145,7 +159,7 @@ __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, i
   constexpr int JG = kWave * KP;
   constexpr int NG = B / JG;
   constexpr int NC = sym_sums<POT>();
-  const int tid = threadIdx.x;
+  const int tid = (int)threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
   // The task's two slots: panel I's sums from J, panel J's sums from I.  For
@@ -156,6 +170,7 @@ __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, i
   // MI355X (2^20 bodies, K = 8: 185.0 against 187.7 ms; 131072 bodies,
   // K = 4: 3.06 against 3.13 ms).
   constexpr bool kHoist = K >= 8;
+  constexpr bool kPace = W == 1;
   float *const part_ij = part + (size_t)map.slot(I, J) * NC * B;
   float *const part_ji = part + (size_t)map.slot(J, I) * NC * B;
 
@@ -211,7 +226,11 @@ __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, i
       // across these points (the empty asm with a memory clobber).
       asm volatile("" ::: "memory");
       float4 y = jt[lane];
-      for (int s0 = 0; s0 < kWave; s0 += U) {
+      // paced tasks take the sweep in two halves, each at its own priority
+      constexpr int kHalves = kPace ? 2 : 1;
+      for (int h = 0; h < kHalves; ++h) {
+      if constexpr (kPace) pace((2 * (2 * g + h)) / NG);
+      for (int s0 = h * (kWave / kHalves); s0 < (h + 1) * (kWave / kHalves); s0 += U) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int k = lane + s0 + u;
@@ -234,8 +253,14 @@ __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, i
           y = yn;
         }
       }
+      }
       // j-side sums of this sweep: add the W waves in ascending order
-      __syncthreads();
+      // W waves add each other's sums: a block barrier; a one-wave task reads
+      // only its own lanes' slots, which one wave's LDS instructions order
+      if constexpr (W > 1)
+        __syncthreads();
+      else
+        asm volatile("" ::: "memory");
       for (int e = tid; e < NC * kWave; e += W * kWave) {
         const int c = e / kWave, l = e % kWave;
         float sum = 0.0f;
@@ -250,10 +275,14 @@ __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, i
         else
           part[((size_t)map.slot(J, I) * NC + c) * B + g * kWave + l] = c < 3 ? -sum : sum;
       }
-      __syncthreads();
+      if constexpr (W > 1)
+        __syncthreads();
+      else
+        asm volatile("" ::: "memory");
     }
   } else {
     for (int g = 0; g < NG; ++g) {
+      if constexpr (kPace) pace((4 * g) / NG);
       float xj[KP], yj[KP], zj[KP], mj[KP], cx[KP], cy[KP], cz[KP], cp[KP];
 #pragma unroll
       for (int p = 0; p < KP; ++p) {
@@ -359,20 +388,23 @@ __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, i
   }
 }
 
-// One block per task (panel pair); PanelOrder gives the pair of each block
-// (every XCD walks a contiguous stretch of tile-ordered pairs).
+// One task (panel pair) per block of W waves.  PanelOrder gives the pair of
+// each block: every XCD walks a contiguous stretch of tile-ordered pairs.
 template <int K, int KP, int W, int OCC, int IL, bool POT, int ML, int JL>
 __global__ __launch_bounds__(W *kWave) __attribute__((amdgpu_waves_per_eu(OCC))) void
 symmetric_task_kernel(const float4 *__restrict__ pm, int n, PanelOrder order, SlotMap map,
                       float eps2, float *__restrict__ part) {
   constexpr int NC = sym_sums<POT>();
+  // one-wave tasks are paced (see pace): a wave starts at the top priority
+  if constexpr (W == 1) __builtin_amdgcn_s_setprio(3);
   __shared__ float csum[JL > 0 ? 1 : W][KP][NC][kWave];
   __shared__ float mis[ML > 0 ? W * ML * kWave : 1];
   __shared__ float4 jtile[JL > 0 ? W * 2 * kWave : 1];
   __shared__ float4 jsum[JL > 0 ? W * 2 * kWave : 1];
   int Ic, Jc;
   long long t;
-  if (!panel_pair_of_block(order, blockIdx.x, Ic, Jc, t)) return;  // whole block: no barrier skipped
+  // the block returns as a whole, so no barrier is skipped
+  if (!panel_pair_of_block(order, blockIdx.x, Ic, Jc, t)) return;
   Ic = __builtin_amdgcn_readfirstlane(Ic);
   Jc = __builtin_amdgcn_readfirstlane(Jc);
   if (Ic == Jc)
@@ -384,44 +416,67 @@ symmetric_task_kernel(const float4 *__restrict__ pm, int n, PanelOrder order, Sl
 }
 
 // The panel sums of one launch's slots (SlotMap map, columns [c0, c1)) added
-// into each touched body's sum in ascending J: a body of a panel K < c0
-// continues the fp32 running sum an earlier chunk left in out[i] and adds
-// its slots J = c0 .. c1 - 1; a body of a panel in [c0, c1) starts from 0
-// and adds J = 0 .. c1 - 1.  The last chunk (c1 = P) writes a_i = G * sum
-// (with POT the fourth sum is phi_i and w = Phi_i = -G phi_i, else w = 0);
-// earlier chunks write the unscaled running sums.  The bodies of panels
-// K >= c1 are not touched: the caller launches min(n, c1 B) threads.
+// into each touched body's sum in ascending J, in two levels: the slots of
+// each block of 32 consecutive panels (J in [32 k, 32 k + 32)) are added in
+// order into a fresh block sum, and the block sums are added in order into
+// the body's sum.  A body of a panel K < c0 continues the fp32 running sum an
+// earlier chunk left in out[i] with the blocks of J = c0 .. c1 - 1; a body of
+// a panel in [c0, c1) starts from 0 with the blocks of J = 0 .. c1 - 1.
+// Chunk bounds are multiples of 32 (or P), so a chunked pass forms the same
+// blocks, in the same order, as the whole pass.  The last chunk (c1 = P)
+// writes a_i = G * sum (with POT the fourth sum is phi_i and w = Phi_i =
+// -G phi_i, else w = 0); earlier chunks write the unscaled running sums.  The
+// bodies of panels K >= c1 are not touched: the caller launches the bodies
+// below min(n, c1 B).
+//
+// A block of 4 waves takes 64 bodies (one panel: B is a multiple of 64) and
+// one component (blockIdx.y); its waves form 4 block sums at a time and
+// wave 0 adds them in order.  That gives small n several waves per SIMD
+// where one thread per body walking all P slots would not.
+constexpr int kReduceWaves = 4;
+
 template <bool POT>
-__global__ __launch_bounds__(256) void symmetric_reduce_kernel(const float *__restrict__ part,
-                                                               int n, int B, SlotMap map,
-                                                               int last, float G,
-                                                               float4 *__restrict__ out) {
+__global__ __launch_bounds__(kReduceWaves *kWave) void symmetric_reduce_kernel(
+    const float *__restrict__ part, int n, int B, SlotMap map, int last, float G,
+    float4 *__restrict__ out) {
   constexpr int NC = sym_sums<POT>();
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  const int K = i / B, b = i % B;
-  float sx = 0.0f, sy = 0.0f, sz = 0.0f, sp = 0.0f;
-  int J = 0;
-  if (K < map.c0) {
-    const float4 r = out[i];
-    sx = r.x;
-    sy = r.y;
-    sz = r.z;
-    sp = r.w;
-    J = map.c0;
-  }
-  const float *s = part + (size_t)map.slot(K, J) * NC * B + b;
+  constexpr int JB = kPanelTile;  // panels per block sum
+  __shared__ float blk[kReduceWaves][kWave];
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+  const int lane = (int)threadIdx.x % kWave;
+  const int i0 = blockIdx.x * kWave;
+  const int i = i0 + lane;
+  const int c = blockIdx.y;
+  const bool live = i < n;
+  const int K = i0 / B;  // the same panel for the 64 bodies
+  const int b = i % B;
+  float *o = reinterpret_cast<float *>(out) + (size_t)i * 4;
+  const int J0 = K < map.c0 ? map.c0 : 0, J1 = map.c1;
+  float sum = 0.0f;
+  if (K < map.c0 && live && wave == 0) sum = o[c];
+  const int nb = (J1 - J0 + JB - 1) / JB;
+  for (int r = 0; r < nb; r += kReduceWaves) {
+    const int jb = r + wave;
+    float p = 0.0f;
+    if (jb < nb && live) {
+      const int ja = J0 + jb * JB, je = min(J1, ja + JB);
+      const float *s = part + ((size_t)map.slot(K, ja) * NC + c) * B + b;
 #pragma unroll 8
-  for (; J < map.c1; ++J, s += (size_t)NC * B) {
-    sx += s[0];
-    sy += s[B];
-    sz += s[2 * B];
-    if constexpr (POT) sp += s[3 * B];
+      for (int J = ja; J < je; ++J, s += (size_t)NC * B) p += s[0];
+    }
+    blk[wave][lane] = p;
+    __syncthreads();
+    if (wave == 0) {
+      for (int w = 0; w < kReduceWaves && r + w < nb; ++w) sum += blk[w][lane];
+    }
+    __syncthreads();
   }
-  if (last)
-    out[i] = make_float4(G * sx, G * sy, G * sz, POT ? -G * sp : 0.0f);
-  else
-    out[i] = make_float4(sx, sy, sz, POT ? sp : 0.0f);
+  if (wave == 0 && live) {
+    // the fourth sum (with the potential) is phi_i, stored as Phi_i = -G phi_i;
+    // without it, w is 0
+    o[c] = last ? (c < 3 ? G * sum : -G * sum) : sum;
+    if (!POT && c == 0) o[3] = 0.0f;
+  }
 }
 
 // (id, K, KP, waves, occupancy target, interleave width, i-masses in LDS,
@@ -433,25 +488,35 @@ __global__ __launch_bounds__(256) void symmetric_reduce_kernel(const float *__re
 //     SIMD): the library's choice above 3e5 bodies;
 //  1  4 i-bodies per lane in 4-wave blocks (1024-body panels, 8 waves per
 //     SIMD): from 77824 to 3e5 bodies;
-//  2  4 i-bodies per lane in one-wave blocks (256-body panels): from 30720
+//  2  4 i-bodies per lane in one-wave blocks (256-body panels): from 21504
 //     to 77824 bodies;
-//  3  2 i-bodies per lane in one-wave blocks (128-body panels): up to 30720
-//     bodies, where larger panels leave too few panel pairs to fill the
-//     chip's 8192 wave slots;
+//  3  2 i-bodies per lane in one-wave blocks (128-body panels): up to
+//     21504 bodies, where larger panels leave too few panel pairs to fill
+//     the chip's 8192 wave slots;
 //  4  variant 0 with the j-state rotated one lane per step by DPP instead of
 //     carried in LDS (7 / K moves per pair): the ablation of the LDS
 //     carriage (the same panel shape; the j-side sums are added in another
 //     order, so it agrees with 0 to rounding).
-// One-wave blocks need no barrier: the wave adds its own j-side sums.
+// A one-wave task needs no barrier: the wave adds its own j-side sums.
+// One-wave tasks are paced (pace): a launch of them is about one round of
+// waves, and the SIMD's oldest-first issue would otherwise finish its waves
+// one after another, leaving the last ones to run nearly alone; raising the
+// priority of the waves that are behind makes them drain together (at 16384
+// bodies 72.0 against 74.8 us for the whole pass, at 24576 bodies with 4
+// i-bodies per lane 133.3 against 145.7 us).  With 4-wave blocks, whose
+// launches are many rounds, it cost 1 to 3.5 % and is not used.
 // Other shapes measured on MI355X and not kept: the rotated carriage with 2
 // j-bodies per lane, 4 to 16 i-bodies per lane, 6 to 8 waves per SIMD, pair
 // interleave widths 2 and 4 (the same as 1 under this register budget), 6 or
-// all 8 i-masses in LDS, and 2 i-bodies per lane in 2-wave blocks.
+// all 8 i-masses in LDS, 2 i-bodies per lane in 2-wave blocks, several
+// one-wave tasks packed into one block (no gain), and loading the next
+// sweep's j-bodies one sweep ahead (up to 5 % slower with 4 i-bodies per
+// lane, no gain with 2).
 #define NBODY_SYM_VARIANTS(X) \
-  X(0, 8, 1, 4, 7, 1, 5, 8)     \
-  X(1, 4, 1, 4, 8, 1, 0, 8)     \
-  X(2, 4, 1, 1, 8, 1, 0, 8)     \
-  X(3, 2, 1, 1, 8, 1, 0, 8)     \
+  X(0, 8, 1, 4, 7, 1, 5, 8)   \
+  X(1, 4, 1, 4, 8, 1, 0, 8)   \
+  X(2, 4, 1, 1, 8, 1, 0, 8)   \
+  X(3, 2, 1, 1, 8, 1, 0, 8)   \
   X(4, 8, 1, 4, 7, 1, 5, 0)
 
 // Variants of the pass that also sums the potential (id, K, KP, waves,
@@ -493,19 +558,21 @@ int symmetric_variant_count(bool pot) {
 }
 
 // Measured on MI355X (force-pass sweeps of every variant on Plummer spheres
-// of 8192 to 524288 bodies), all with the j-state in LDS: 2 i-bodies per
-// lane in one-wave blocks up to ~30000 bodies (86.8 us at 16384 against
-// 102.0 us for 4 i-bodies and 100.4 us for the one-sided pass; 193.7 against
-// 200.4 us at 28672, 255.4 against 245.6 us at 32768), 4 in one-wave blocks
-// up to ~78000 (1.035 against 1.053 ms at 73728, 1.288 against 1.236 ms at
-// 81920), 4 in 4-wave blocks up to ~3e5 (12.07 against 12.29 ms at 262144,
-// the same at 327680), 8 in 4-wave blocks above (26.7 against 27.0 ms at
-// 393216, 46.9 against 47.8 ms at 2^19).  The potential variants follow the
-// same split, with the same panel shapes and j-state carriage, so their xyz
-// equal the plain pass's.
+// of 8192 to 524288 bodies, each call timed whole: panel pairs and reduce),
+// all with the j-state in LDS: 2 i-bodies per lane in one-wave blocks up to
+// ~21000 bodies (74.9 us at 16384 against 88.5 us for 4 i-bodies and 95.5 us
+// for the one-sided pass; 105.5 against 110.4 us at 20480, 122.1 against
+// 112.5 us at 22528), 4 in one-wave blocks up to ~78000 (0.826 against 0.855
+// ms for 4-wave blocks at 65536, 1.038 against 1.045 ms at 73728, 1.289
+// against 1.228 ms at 81920), 4 in 4-wave blocks up to ~3e5 (3.04 against
+// 3.30 ms at 131072; 12.07 against 12.29 ms at 262144, the same at 327680),
+// 8 in 4-wave blocks above (26.7 against 27.0 ms at 393216, 46.9 against
+// 47.8 ms at 2^19).  The potential variants follow the same split, with the
+// same panel shapes and j-state carriage, so their xyz equal the plain
+// pass's.
 int symmetric_variant_for_n(int64_t n, bool pot) {
   (void)pot;
-  return n <= 30720 ? 3 : n <= 77824 ? 2 : n <= 300000 ? 1 : 0;
+  return n <= 21504 ? 3 : n <= 77824 ? 2 : n <= 300000 ? 1 : 0;
 }
 
 int symmetric_panel(int v, bool pot) {
@@ -563,11 +630,11 @@ static hipError_t launch_tasks_columns(const float *posmass, int n, float eps2, 
   const float4 *pm = reinterpret_cast<const float4 *>(posmass);
   if (!pot) {
     switch (v) {
-#define X(id, K, KP, W, OCC, IL, ML, JL)                                               \
-  case id:                                                                             \
-    hipLaunchKernelGGL((symmetric_task_kernel<K, KP, W, OCC, IL, false, ML, JL>),      \
-                       dim3((unsigned)blocks), dim3(W * kWave), 0, stream, pm, n, order, map, \
-                       eps2, part);                                                    \
+#define X(id, K, KP, W, OCC, IL, ML, JL)                                                      \
+  case id:                                                                                     \
+    hipLaunchKernelGGL((symmetric_task_kernel<K, KP, W, OCC, IL, false, ML, JL>),              \
+                       dim3((unsigned)blocks), dim3(W * kWave), 0, stream, pm, n, order, map,  \
+                       eps2, part);                                                            \
     break;
       NBODY_SYM_VARIANTS(X)
 #undef X
@@ -576,11 +643,11 @@ static hipError_t launch_tasks_columns(const float *posmass, int n, float eps2, 
     }
   } else {
     switch (v) {
-#define X(id, K, KP, W, OCC, ML, JL)                                                   \
-  case id:                                                                             \
-    hipLaunchKernelGGL((symmetric_task_kernel<K, KP, W, OCC, 1, true, ML, JL>),        \
-                       dim3((unsigned)blocks), dim3(W * kWave), 0, stream, pm, n, order, map, \
-                       eps2, part);                                                    \
+#define X(id, K, KP, W, OCC, ML, JL)                                                          \
+  case id:                                                                                     \
+    hipLaunchKernelGGL((symmetric_task_kernel<K, KP, W, OCC, 1, true, ML, JL>),                \
+                       dim3((unsigned)blocks), dim3(W * kWave), 0, stream, pm, n, order, map,  \
+                       eps2, part);                                                            \
     break;
       NBODY_SYM_POT_VARIANTS(X)
 #undef X
@@ -602,13 +669,13 @@ static hipError_t launch_reduce_columns(int n, float G, float *accel, int v, boo
   const int last = c1 == P;
   const float *part = reinterpret_cast<const float *>(workspace);
   float4 *out = reinterpret_cast<float4 *>(accel);
-  const dim3 grid((touched + 255) / 256);
+  const dim3 grid((touched + kWave - 1) / kWave, pot ? 4 : 3);
   if (pot)
-    hipLaunchKernelGGL(symmetric_reduce_kernel<true>, grid, dim3(256), 0, stream, part, touched,
-                       B, map, last, G, out);
+    hipLaunchKernelGGL(symmetric_reduce_kernel<true>, grid, dim3(kReduceWaves * kWave), 0,
+                       stream, part, touched, B, map, last, G, out);
   else
-    hipLaunchKernelGGL(symmetric_reduce_kernel<false>, grid, dim3(256), 0, stream, part, touched,
-                       B, map, last, G, out);
+    hipLaunchKernelGGL(symmetric_reduce_kernel<false>, grid, dim3(kReduceWaves * kWave), 0,
+                       stream, part, touched, B, map, last, G, out);
   return hipGetLastError();
 }
 

@@ -62,7 +62,8 @@ int main() {
     // a chunk's launch take exactly the pairs with J in [c0, c1), each once;
     // every slot of the chunk's SlotMap is written by exactly one task side
     // and lies in [0, slots()); and the reduces, chunk after chunk, add each
-    // panel's sums for J = 0 .. P-1 once each, in ascending J.
+    // panel's sums for J = 0 .. P-1 once each, in ascending J, in blocks of 32
+    // panels that start at multiples of 32.
     for (int C : {32, 64, 96, 128}) {
       std::vector<int> next_j(P, 0);  // the J each panel's running sum expects next
       for (int c0 = 0; c0 < P; c0 += C) {
@@ -104,9 +105,14 @@ int main() {
             break;
           }
         // the reduce: panels K < c0 add J in [c0, c1), panels in the chunk
-        // start afresh and add J in [0, c1); slots of consecutive J adjacent
+        // start afresh and add J in [0, c1); slots of consecutive J adjacent;
+        // its blocks of 32 panels start at multiples of 32, as in the whole pass
         for (int K = 0; K < c1; ++K) {
           const int jfirst = K < c0 ? c0 : 0;
+          if (jfirst % kPanelTile != 0) {
+            std::printf("P=%d C=%d: panel %d block sums start at J=%d\n", P, C, K, jfirst);
+            ++bad;
+          }
           if (K >= c0 && next_j[K] != 0) {
             std::printf("P=%d C=%d: panel %d starts again at chunk %d\n", P, C, K, c0);
             ++bad;

@@ -371,10 +371,10 @@ def test_symmetric_two_phases_equal_one_call(n, variant):
     assert np.array_equal(out.cpu().numpy(), one)
 
 
-@pytest.mark.parametrize("n", [30720, 30721, 77825, 131072, 300001])
+@pytest.mark.parametrize("n", [21504, 21505, 77825, 131072, 300001])
 def test_symmetric_default_variant_at_switch_sizes(n):
     """The library's choice on both sides of its switches (one-wave blocks of
-    2 and 4 i-bodies per lane, 4-wave blocks of 4 and 8, switching at 30720,
+    2 and 4 i-bodies per lane, 4-wave blocks of 4 and 8, switching at 21504,
     77824 and 3e5 bodies): lognormal masses, sampled rows including the first
     and last 64 against the oracle, every row against the one-sided pass, and
     a repeat bitwise."""
