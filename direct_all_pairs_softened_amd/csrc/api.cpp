@@ -34,7 +34,15 @@ int check_consts(float G, float eps2) {
   return NBODY_OK;
 }
 
-int hip_status(hipError_t e) { return e == hipSuccess ? NBODY_OK : NBODY_ERR_HIP; }
+// A failed runtime call is reported through the status alone: its error is
+// also consumed from the thread's last-error state, so that the caller's own
+// next error check does not see it again (a fault that leaves the device
+// unusable stays reported by every later call anyway).
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return NBODY_OK;
+  (void)hipGetLastError();
+  return NBODY_ERR_HIP;
+}
 
 hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
@@ -465,7 +473,8 @@ int nbody_energy_static(const float *posmass, const float *vel, int64_t n, float
   if (overlap(stats_out, sb, posmass, bytes) || overlap(stats_out, sb, vel, bytes))
     return NBODY_ERR_ALIAS;
   void *scratch = nullptr;
-  if (nbody::energy_static_scratch(&scratch) != hipSuccess) return NBODY_ERR_HIP;
+  const hipError_t se = nbody::energy_static_scratch(&scratch);
+  if (se != hipSuccess) return hip_status(se);
   return hip_status(nbody::launch_energy(posmass, vel, (int)n, G, eps2, scratch, stats_out,
                                          as_stream(stream)));
 }
@@ -514,7 +523,8 @@ constexpr int kMaxTimedReps = 1 << 16;
 // NBODY_OK when `stream` is not being captured into a graph.
 int not_capturing(hipStream_t stream) {
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return NBODY_ERR_HIP;
+  const hipError_t e = hipStreamIsCapturing(stream, &cs);
+  if (e != hipSuccess) return hip_status(e);
   return cs == hipStreamCaptureStatusNone ? NBODY_OK : NBODY_ERR_INVALID_ARG;
 }
 
@@ -545,9 +555,10 @@ int nbody_timer_create(int marks, nbody_timer **timer_out) {
   if (!timer_out || marks < 1 || marks > kMaxTimerMarks) return NBODY_ERR_INVALID_ARG;
   *timer_out = nullptr;
   nbody_timer *t = new nbody_timer;
-  if (create_events(t->ev, marks) != hipSuccess) {
+  const hipError_t e = create_events(t->ev, marks);
+  if (e != hipSuccess) {
     delete t;
-    return NBODY_ERR_HIP;
+    return hip_status(e);
   }
   *timer_out = t;
   return NBODY_OK;

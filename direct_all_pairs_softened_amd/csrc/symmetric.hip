@@ -25,8 +25,11 @@
 //    wave's LDS; each step a lane reads the body it meets, sums its K pairs'
 //    j-side terms in registers, then adds them to the body's slot (a read, 3
 //    adds and a write: the adds dual-issue, and no DPP moves are left).
-// Diagonal tasks (I = J) use the one-sided sum (j over the whole panel,
-// self term exactly 0) and no j-side sums.
+// Diagonal tasks (I = J) of the 4-wave variants use the one-sided sum (j
+// over the whole panel, self term exactly 0) and no j-side sums; those of the
+// one-wave variants are pair-symmetric within the panel (sym_diag_task), each
+// pair once in the one-sided pass's mass-first form, at about half the
+// cost.
 //
 // Output of a task: panel I's sums from panel J and, for I < J, panel J's
 // sums from panel I, each in its own workspace slot of NC x B floats (NC = 3
@@ -388,6 +391,102 @@ __device__ __forceinline__ void sym_task(const float4 *__restrict__ pm, int n, i
   }
 }
 
+// A diagonal panel pair (I, I) of a one-wave task, each unordered pair of the
+// panel met once (the off-diagonal sweep would meet every pair twice).  The
+// panel's j-groups g (64 bodies each) are taken from the last to the first;
+// group g is staged twice in a row in the wave's LDS tile with zeroed slots,
+// as in the off-diagonal sweep.  The lane's i-bodies of the groups q < g meet
+// all 64 j-bodies (steps 0 .. 63), and its i-body of group g meets the
+// bodies 1 .. 32 lanes ahead (at 32 only lanes 0 .. 31, so that each pair of
+// the group is met once and no body meets itself).  i-side terms gather in
+// registers, j-side terms in the group's LDS slots under the same in-order
+// rule as the off-diagonal sweep.  After group g both sums of its bodies are
+// complete (later groups are earlier ones, which meet g only as j-bodies), so
+// its panel sums are written then: i-side minus j-side (the potential: plus).
+// About half the work of an off-diagonal task.
+template <int K, bool POT>
+__device__ __forceinline__ void sym_diag_task(const float4 *__restrict__ pm, int n, int I,
+                                              SlotMap map, float eps2, float *__restrict__ part,
+                                              float4 *jt, float4 *js) {
+  constexpr int B = kWave * K;
+  constexpr int NC = sym_sums<POT>();
+  const int lane = (int)threadIdx.x % kWave;
+  float xi[K], yi[K], zi[K], mi[K], ax[K], ay[K], az[K], ap[K];
+#pragma unroll
+  for (int q = 0; q < K; ++q) {
+    const int i = I * B + q * kWave + lane;
+    const float4 b = pm[i < n ? i : n - 1];
+    xi[q] = b.x;
+    yi[q] = b.y;
+    zi[q] = b.z;
+    mi[q] = i < n ? b.w : 0.0f;
+    ax[q] = 0.0f;
+    ay[q] = 0.0f;
+    az[q] = 0.0f;
+    ap[q] = 0.0f;
+  }
+  // one pair: this lane's i-body q and the j-body in tile entry k, the j-side
+  // term added into slot k (q is a constant once the loops are unrolled)
+  auto pair = [&](int q, int k) {
+    const float4 y = jt[k];
+    const float dx = y.x - xi[q];
+    const float dy = y.y - yi[q];
+    const float dz = y.z - zi[q];
+    float w = __builtin_fmaf(dx, dx, eps2);
+    w = __builtin_fmaf(dy, dy, w);
+    w = __builtin_fmaf(dz, dz, w);
+    const float inv = __builtin_amdgcn_rsqf(w);
+    const float inv2 = inv * inv;
+    // mass first, as in the one-sided pass: the zero-mass copies of body n - 1
+    // that pad the last panel sit on that body, and a zero mass must turn
+    // their terms into exact zeros for any eps2 > 0
+    const float sj = (y.w * inv) * inv2;
+    ax[q] = __builtin_fmaf(sj, dx, ax[q]);
+    ay[q] = __builtin_fmaf(sj, dy, ay[q]);
+    az[q] = __builtin_fmaf(sj, dz, az[q]);
+    if constexpr (POT) ap[q] = __builtin_fmaf(y.w, inv, ap[q]);
+    const float si = (mi[q] * inv) * inv2;
+    float4 c = js[k];
+    c.x = __builtin_fmaf(si, dx, c.x);
+    c.y = __builtin_fmaf(si, dy, c.y);
+    c.z = __builtin_fmaf(si, dz, c.z);
+    if constexpr (POT) c.w = __builtin_fmaf(mi[q], inv, c.w);
+    js[k] = c;
+    // the slot's next access is another lane's, one pair later
+    asm volatile("" ::: "memory");
+  };
+  float *row = part + (size_t)map.slot(I, I) * NC * B;
+#pragma unroll
+  for (int g = K - 1; g >= 0; --g) {
+    const int j = I * B + g * kWave + lane;
+    const float4 b = pm[j < n ? j : n - 1];
+    const float4 jb = make_float4(b.x, b.y, b.z, j < n ? b.w : 0.0f);
+    jt[lane] = jb;
+    jt[lane + kWave] = jb;
+    js[lane] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    js[lane + kWave] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int q = 0; q < g; ++q) {
+#pragma unroll 8
+      for (int s = 0; s < kWave; ++s) pair(q, lane + s);
+    }
+#pragma unroll 8
+    for (int s = 1; s < kWave / 2; ++s) pair(g, lane + s);
+    if (lane < kWave / 2) pair(g, lane + kWave / 2);
+    asm volatile("" ::: "memory");
+    // group g's panel sums; a lane reads only its own bodies' slots
+    const float4 lo = js[lane], hi = js[lane + kWave];
+    const int bg = g * kWave + lane;
+    row[bg] = ax[g] - (lo.x + hi.x);
+    row[B + bg] = ay[g] - (lo.y + hi.y);
+    row[2 * B + bg] = az[g] - (lo.z + hi.z);
+    if constexpr (POT) row[3 * B + bg] = ap[g] + (lo.w + hi.w);
+    // the next group overwrites the tile after every lane's reads
+    asm volatile("" ::: "memory");
+  }
+}
+
 // One task (panel pair) per block of W waves.  PanelOrder gives the pair of
 // each block: every XCD walks a contiguous stretch of tile-ordered pairs.
 template <int K, int KP, int W, int OCC, int IL, bool POT, int ML, int JL>
@@ -407,10 +506,13 @@ symmetric_task_kernel(const float4 *__restrict__ pm, int n, PanelOrder order, Sl
   if (!panel_pair_of_block(order, blockIdx.x, Ic, Jc, t)) return;
   Ic = __builtin_amdgcn_readfirstlane(Ic);
   Jc = __builtin_amdgcn_readfirstlane(Jc);
-  if (Ic == Jc)
-    sym_task<K, KP, W, IL, POT, ML, JL, true>(pm, n, Ic, Jc, map, eps2, part, csum, mis, jtile,
-                                              jsum);
-  else
+  if (Ic == Jc) {
+    if constexpr (W == 1 && JL > 0)
+      sym_diag_task<K, POT>(pm, n, Ic, map, eps2, part, jtile, jsum);
+    else
+      sym_task<K, KP, W, IL, POT, ML, JL, true>(pm, n, Ic, Jc, map, eps2, part, csum, mis, jtile,
+                                                jsum);
+  } else
     sym_task<K, KP, W, IL, POT, ML, JL, false>(pm, n, Ic, Jc, map, eps2, part, csum, mis, jtile,
                                                jsum);
 }

@@ -28,7 +28,10 @@
  *  - n is the body count: 0 <= n <= NBODY_MAX_N.  n == 0 is a no-op that
  *    returns NBODY_OK and touches no pointer.
  *  - Arguments are validated before anything is enqueued; on any error
- *    nothing is enqueued.  A failed launch returns NBODY_ERR_HIP.
+ *    nothing is enqueued.  A failed launch or runtime call returns
+ *    NBODY_ERR_HIP, and its error is consumed from HIP's per-thread
+ *    last-error state (hipGetLastError), so the caller's next check does not
+ *    report it a second time.
  *  - NaN or Inf inside the arrays are not checked; they propagate.
  *  - Outputs are in input order: row i of an output belongs to body i.
  *  - Results are bitwise reproducible for a given (n, entry point, variant):
@@ -227,7 +230,12 @@ size_t nbody_accel_splitj_tree_workspace_bytes(int64_t n, int64_t j_chunk, int t
  * both bodies), so besides nbody_accel's limit eps2 must stay above about
  * 2.1e-26 whatever the masses: below it inv^3 overflows for coincident
  * bodies in different panels, and both their rows come out NaN (inf * 0).
- * Diagonal panel pairs use nbody_accel's mass-first form.  Not checked.
+ * A diagonal panel pair (I, I) keeps nbody_accel's mass-first form, so
+ * coincident bodies in one panel follow nbody_accel's limit: in the 4-wave
+ * variants (0, 1, 4) it is summed one-sidedly, j = i included; in the
+ * one-wave variants (2, 3) each pair of the panel is met once and j = i is
+ * never formed, so the self term, and its overflow, do not arise.  Not
+ * checked.
  * Other arguments as nbody_accel.  NBODY_ERR_INVALID_ARG also when the
  * panel pairs exceed 2^31 - 1 (n beyond ~1.3e8). */
 int nbody_accel_symmetric(const float *posmass, int64_t n, float G, float eps2,
@@ -303,8 +311,9 @@ int nbody_accel_symmetric_reduce(int64_t n, float G, float *accel_out, int varia
  *   accel_out[i] = (ax, ay, az, Phi_i),
  *   Phi_i = -G sum_{j != i} m_j / sqrt(|x_j - x_i|^2 + eps^2).
  * Each unordered pair adds m_j inv to body i's sum and m_i inv to body j's
- * (two more multiply-adds per pair); the j = i pair is left out by an index
- * test inside the diagonal panel pairs.  The potential sums follow the
+ * (two more multiply-adds per pair); the j = i pair is left out (by an
+ * index test in the one-sided diagonal panel pairs of the 4-wave variants;
+ * the one-wave variants never form it).  The potential sums follow the
  * acceleration's order (per panel pair, then panel pairs in ascending
  * order).  Its variants are a table of their own (ids below).  The xyz
  * outputs are bitwise equal to nbody_accel_symmetric's for a variant of the

@@ -93,8 +93,13 @@ def test_timer_brackets_work_on_its_stream():
         assert one > 0 and two > 0
         assert abs(t.elapsed_ms(0, 2) - (one + two)) <= 1e-2 * (one + two) + 1e-3
         assert t.elapsed_ms(1, 1) == 0.0
-        # a mark that was never recorded cannot be read
+        # a mark that was never recorded cannot be read; the failure is
+        # reported once, by the status, and not left behind for the caller's
+        # next HIP call
         with pytest.raises(nb.NBodyError):
             t.elapsed_ms(0, 3)
+        after = torch.full((4,), 2.0, device=DEV)
+        torch.cuda.synchronize()
+        assert after.sum().item() == 8.0
     finally:
         t.close()
