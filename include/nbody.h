@@ -215,7 +215,9 @@ size_t nbody_accel_splitj_tree_workspace_bytes(int64_t n, int64_t j_chunk, int t
  * panels of nbody_accel_symmetric_panel(variant) bodies; a panel pair (I, J)
  * writes panel I's sums from J and panel J's sums from I into the
  * workspace, and a second kernel adds, for each body, the P panel sums in
- * ascending panel order and multiplies by G.  The order differs from
+ * blocks of 32 panels (each block's sums in ascending panel order into a
+ * fresh block sum, the block sums in ascending order) and multiplies by G.
+ * The order differs from
  * nbody_accel's, so the two agree to rounding, not bitwise; variants that
  * carry the second body's share differently (registers or LDS) also agree
  * to rounding only.
@@ -256,8 +258,9 @@ int nbody_accel_symmetric_variant_for_n(int64_t n);
  * the pairs with J in a range of chunk_panels panels (ascending ranges);
  * after each chunk's panel-pair kernel, a reduce kernel adds that chunk's
  * panel sums into each touched body's fp32 running sum (kept in accel_out
- * between chunks) in ascending panel order, and the last chunk multiplies by
- * G.  Each body's panel sums are therefore added in the same order as by
+ * between chunks) in the same blocks of 32 panels, ascending (chunk bounds
+ * are multiples of 32), and the last chunk multiplies by G.  Each body's
+ * panel sums are therefore added in the same order as by
  * nbody_accel_symmetric, and accel_out is bitwise equal to its result for
  * the same variant, whatever chunk_panels.
  * Consecutive chunks run on two queues, in two halves of the workspace:
@@ -293,7 +296,7 @@ size_t nbody_accel_symmetric_chunked_workspace_bytes(int64_t n, int variant, int
  * its own).  nbody_accel_symmetric_tasks runs the panel-pair kernel: it reads
  * posmass and writes every panel sum into the workspace.
  * nbody_accel_symmetric_reduce runs the second kernel: it adds each body's
- * panel sums in ascending panel order into accel_out, times G.  The reduce
+ * panel sums (blocks of 32 panels, ascending) into accel_out, times G.  The reduce
  * must be given the same n, variant and workspace, with the contents the
  * tasks call left, on the same stream or one ordered after it; the pair
  * then gives accel_out bitwise equal to nbody_accel_symmetric's.  Arguments,
