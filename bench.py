@@ -293,6 +293,13 @@ def suite(nb, torch, names):
                           "energy_drift": abs(e1["E"] - e0["E"]) / abs(e0["E"]),
                           "momentum_change": dp}
             del vel
+        if w.n <= 20000:
+            # launch-bound sizes: the library's step loop, eager and as a HIP graph
+            fastest = min(("one_sided", "symmetric"),
+                          key=lambda k: next(v["ms_median"] for f, v in force.items()
+                                             if f.startswith(k)))
+            out["kdk_run"] = kdk_run_timing(nb, torch, w, pm_np, vel_np, fastest, sym_ws, sv,
+                                            tv)
         if name == "plummer1m":
             vel = torch.from_numpy(vel_np).to(dev)
             sv_ws = sym_ws
@@ -307,6 +314,59 @@ def suite(nb, torch, names):
         print(json.dumps(out), flush=True)
         del pm, acc, sym_ws
         torch.cuda.empty_cache()
+
+
+def kdk_run_timing(nb, torch, w, pm_np, vel_np, best, sym_ws, sv, tv, steps=200):
+    """`steps` kick-drift-kick steps from the workload's initial state, run by
+    the library's loop (nbody_kdk_run) and as the calls made one by one
+    (nbody_leapfrog_step, the force pass, nbody_kick): ms per step between
+    events around the whole run.  The two final states must be bitwise
+    equal."""
+    dev = torch.device("cuda:0")
+    dt = w.dt if w.dt > 0 else 1e-3   # a workload without dynamics of its own
+    sym = best == "symmetric"
+    kind = nb.NBODY_PASS_SYMMETRIC if sym else nb.NBODY_PASS_ONE_SIDED
+    variant = sv if sym else tv
+    ws = sym_ws if sym else None
+
+    def fpass(pm, acc):
+        if sym:
+            nb.nbody_accel_symmetric(pm, w.G, w.eps2, acc, ws, variant)
+        else:
+            nb.nbody_accel_variant(pm, w.G, w.eps2, acc, variant)
+
+    res, finals = {}, {}
+    # untimed: the first steps after a change of work run slow (clocks, caches)
+    pm = torch.from_numpy(pm_np).to(dev)
+    vel = torch.from_numpy(vel_np).to(dev)
+    acc = torch.empty_like(pm)
+    fpass(pm, acc)
+    nb.nbody_kdk_run(pm, vel, acc, w.G, w.eps2, dt, steps // 4, kind, variant, ws)
+    torch.cuda.synchronize()
+    for how in ("library", "calls"):
+        pm = torch.from_numpy(pm_np).to(dev)
+        vel = torch.from_numpy(vel_np).to(dev)
+        acc = torch.empty_like(pm)
+        fpass(pm, acc)
+        torch.cuda.synchronize()
+        t = nb.Timer(2)
+        t.mark(0)
+        if how == "library":
+            nb.nbody_kdk_run(pm, vel, acc, w.G, w.eps2, dt, steps, kind, variant, ws)
+        else:
+            for _ in range(steps):
+                nb.nbody_leapfrog_step(pm, vel, acc, dt)
+                fpass(pm, acc)
+                nb.nbody_kick(vel, acc, 0.5 * dt)
+        t.mark(1)
+        res[how] = t.elapsed_ms(0, 1) / steps
+        t.close()
+        finals[how] = [x.cpu() for x in (pm, vel, acc)]
+    same = all(torch.equal(a, b) for a, b in zip(finals["library"], finals["calls"]))
+    if not same:
+        raise AssertionError("nbody_kdk_run differs from the calls made one by one")
+    return {"steps": steps, "force_pass": best, "library_ms_per_step": res["library"],
+            "calls_ms_per_step": res["calls"], "bitwise_equal": same}
 
 
 def suite_report(path):
@@ -327,6 +387,15 @@ def suite_report(path):
             out.append("| %s | %d x %g | %s | %.4g | %.2e | %.2e |" % (
                 r["workload"], run["steps"], run["dt"], run["force_pass"],
                 run["step_ms_median"], run["energy_drift"], run["momentum_change"]))
+    runs = [r for r in recs if r.get("kdk_run")]
+    if runs:
+        out += ["", "| workload | steps | force pass | nbody_kdk_run ms per step | "
+                "calls one by one ms per step | bitwise equal |", "|---|---|---|---|---|---|"]
+        for r in runs:
+            k = r["kdk_run"]
+            out.append("| %s | %d | %s | %.4g | %.4g | %s |" % (
+                r["workload"], k["steps"], k["force_pass"], k["library_ms_per_step"],
+                k["calls_ms_per_step"], "yes" if k["bitwise_equal"] else "no"))
     print("\n".join(out))
 
 

@@ -47,7 +47,7 @@ EXPORTS = (
     "nbody_accel_symmetric_potential_variant_count", "nbody_accel_symmetric_potential_panel",
     "nbody_accel_symmetric_potential_variant_for_n",
     "nbody_accel_f3aos", "nbody_accel_soa",
-    "nbody_leapfrog_step", "nbody_kick",
+    "nbody_leapfrog_step", "nbody_kick", "nbody_kdk_run",
     "nbody_energy", "nbody_energy_workspace_bytes", "nbody_energy_static",
     "nbody_timer_create", "nbody_timer_mark", "nbody_timer_elapsed_ms", "nbody_timer_destroy",
     "nbody_time_accel",
@@ -121,6 +121,8 @@ def load_library(path: str | None = None):
         "nbody_accel_soa": (c_int, [vp, vp, vp, vp, c_i64, c_f, c_f, vp, vp, vp, vp]),
         "nbody_leapfrog_step": (c_int, [vp, vp, vp, c_f, c_i64, vp]),
         "nbody_kick": (c_int, [vp, vp, c_f, c_i64, vp]),
+        "nbody_kdk_run": (c_int, [vp, vp, vp, c_i64, c_f, c_f, c_f, c_int, c_int, c_int, vp,
+                                  c_sz, vp]),
         "nbody_energy": (c_int, [vp, vp, c_i64, c_f, c_f, vp, c_sz, vp, vp]),
         "nbody_energy_workspace_bytes": (c_sz, [c_i64]),
         "nbody_energy_static": (c_int, [vp, vp, c_i64, c_f, c_f, vp, vp]),
@@ -461,6 +463,27 @@ def nbody_kick(vel, accel, h: float, stream=None):
     _check(load_library().nbody_kick(_f32(vel, "vel", (4,)), _f32(accel, "accel", (4,)), h, n,
                                       _stream(stream)),
            "nbody_kick")
+
+
+def nbody_kdk_run(posmass, vel, accel, G: float, eps2: float, dt: float, steps: int,
+                  pass_kind: int = 0, variant: int = -1, workspace=None, stream=None):
+    """``steps`` kick-drift-kick steps run by the library (bitwise the same as
+    nbody_leapfrog_step, the force pass and nbody_kick called step by step).
+    accel holds a(x) on entry and a(x_final) on return; pass_kind is one of
+    NBODY_PASS_*."""
+    n = _n_of(posmass)
+    if _n_of(vel) != n or _n_of(accel) != n:
+        raise ValueError("posmass, vel and accel must have N rows")
+    if workspace is None:
+        ws, nbytes = ctypes.c_void_p(), 0
+    else:
+        ws = _dev(workspace, "workspace")
+        nbytes = workspace.numel() * workspace.element_size()
+    _check(load_library().nbody_kdk_run(_f32(posmass, "posmass", (4,)), _f32(vel, "vel", (4,)),
+                                        _f32(accel, "accel", (4,)), n, G, eps2, dt, int(steps),
+                                        int(pass_kind), int(variant), ws, nbytes,
+                                        _stream(stream)),
+           "nbody_kdk_run")
 
 
 def nbody_energy_workspace_bytes(n: int) -> int:

@@ -632,4 +632,47 @@ int nbody_time_accel(const float *posmass, int64_t n, float G, float eps2, float
   return hip_status(e);
 }
 
+int nbody_kdk_run(float *posmass, float *vel, float *accel, int64_t n, float G, float eps2,
+                  float dt, int steps, int pass, int variant, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+  if (steps < 0 || !isfinite(dt)) return NBODY_ERR_INVALID_ARG;
+  const bool one_sided = pass == NBODY_PASS_ONE_SIDED;
+  const bool pot = pass == NBODY_PASS_SYMMETRIC_POTENTIAL;
+  if (!one_sided && pass != NBODY_PASS_SYMMETRIC && !pot) return NBODY_ERR_INVALID_ARG;
+  int v;
+  if (one_sided) {
+    v = variant < 0 ? nbody::force_variant_for_n(n) : variant;
+    if (int s = force_aos4_check(posmass, n, G, eps2, accel, v)) return s;
+  } else {
+    v = sym_variant(variant, n, pot);
+    if (int s = sym_check(posmass, n, G, eps2, accel, v, pot, workspace, workspace_bytes, true,
+                          true))
+      return s;
+  }
+  if (n == 0 || steps == 0) return NBODY_OK;
+  if (!vel) return NBODY_ERR_INVALID_ARG;
+  if (!aligned(vel, 16)) return NBODY_ERR_ALIGNMENT;
+  const size_t bytes = (size_t)n * 16;
+  if (overlap(vel, bytes, posmass, bytes) || overlap(vel, bytes, accel, bytes) ||
+      (!one_sided && overlap(vel, bytes, workspace, workspace_bytes)))
+    return NBODY_ERR_ALIAS;
+  const hipStream_t st = as_stream(stream);
+  const int ni = (int)n;
+  BodyArrays b;
+  b.posmass = posmass;
+  b.accel4 = accel;
+  // step 1 opens with a kick-drift; steps 1 .. steps - 1 end with the force
+  // pass and the fused closing kick + next kick-drift; the last step with
+  // the force pass and a closing kick
+  hipError_t e = nbody::launch_leapfrog(posmass, vel, accel, dt, ni, st);
+  for (int s = 1; s <= steps && e == hipSuccess; ++s) {
+    e = one_sided ? nbody::launch_force(v, Layout::Aos4, b, ni, 0, ni, G, eps2, st)
+                  : nbody::launch_symmetric(posmass, ni, G, eps2, accel, v, pot, workspace, st);
+    if (e == hipSuccess)
+      e = s < steps ? nbody::launch_kick_leapfrog(posmass, vel, accel, dt, ni, st)
+                    : nbody::launch_kick(vel, accel, 0.5f * dt, ni, st);
+  }
+  return hip_status(e);
+}
+
 }  // extern "C"

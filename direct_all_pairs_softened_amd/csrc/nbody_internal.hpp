@@ -86,6 +86,9 @@ hipError_t launch_symmetric_chunked(const float *posmass, int n, float G, float 
                                     void *workspace, hipStream_t stream);
 
 // Integrator.
+// closing half-kick of a step and kick-drift of the next, fused (h = dt / 2)
+hipError_t launch_kick_leapfrog(float *posmass, float *vel, const float *accel, float dt, int n,
+                                hipStream_t stream);
 hipError_t launch_leapfrog(float *posmass, float *vel, const float *accel, float dt, int n,
                            hipStream_t stream);
 hipError_t launch_kick(float *vel, const float *accel, float h, int n, hipStream_t stream);

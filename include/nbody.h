@@ -372,6 +372,34 @@ int nbody_leapfrog_step(float *posmass, float *vel, const float *accel,
 int nbody_kick(float *vel, const float *accel, float h, int64_t n,
                void *stream);
 
+/* `steps` kick-drift-kick steps (README section 1.3, read as above: the
+ * printed kick and drift, a force pass, the closing half kick) run by the
+ * library: exactly nbody_leapfrog_step, the force pass and nbody_kick with
+ * h = dt/2, step after step, except that the closing half kick of a step and
+ * the kick-drift of the next, which use the same accelerations, run as one
+ * kernel doing the same operations in the same order.  The result is
+ * bitwise that of the calls made one by one.
+ *   posmass, vel  [n] float4, in place (masses and vel.w unchanged).
+ *   accel         [n] float4: on entry the accelerations at the current
+ *                 positions (for example from a force pass); on return those
+ *                 at the final positions.  With NBODY_PASS_SYMMETRIC_POTENTIAL
+ *                 accel.w carries Phi_i on return (it is not read).
+ *   pass          one of the NBODY_PASS_* values defined with
+ *                 nbody_time_accel below: the one-sided pass
+ *                 (nbody_accel_variant), the pair-symmetric pass (whole, not
+ *                 chunked) or that pass with the potential; variant -1 for the
+ *                 library's choice; workspace as that pass needs (unused
+ *                 by the one-sided pass).
+ * Like every compute entry point it allocates nothing and does not
+ * synchronise, and it records no memset, so a caller may capture it into a
+ * HIP graph on a stream of its own and replay it.
+ * steps == 0 or n == 0 is a no-op.  The arrays must be pairwise disjoint
+ * and disjoint from the workspace.  Other arguments and errors as the force
+ * pass and nbody_leapfrog_step. */
+int nbody_kdk_run(float *posmass, float *vel, float *accel, int64_t n, float G, float eps2,
+                  float dt, int steps, int pass, int variant, void *workspace,
+                  size_t workspace_bytes, void *stream);
+
 /* Energy and momentum.  stats_out (device, 8 doubles) receives
  *   {K, W, K + W, Px, Py, Pz, M, 0}
  * with K = sum m |v|^2 / 2, P = sum m v, M = sum m and

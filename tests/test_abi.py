@@ -415,3 +415,31 @@ def test_symmetric_chunked_sizes_and_validation(lib):
     assert f(vp(A), 1000, 1.0, 0.0, vp(B), -1, 32, vp(C), need, None) == nb.NBODY_ERR_INVALID_ARG
     assert f(vp(A), 1000, 1.0, 1e-4, vp(A), -1, 32, vp(C), need, None) == nb.NBODY_ERR_ALIAS
     assert f(vp(A), 0, 1.0, 1e-4, vp(B), -1, 32, None, 0, None) == nb.NBODY_OK
+
+
+def test_kdk_run_validation(lib):
+    """nbody_kdk_run checks its steps, dt and pass, the force pass's own
+    arguments and vel before it launches anything; steps == 0 and n == 0 are
+    no-ops."""
+    f = lib.nbody_kdk_run
+    INV = nb.NBODY_ERR_INVALID_ARG
+    one, sym = nb.NBODY_PASS_ONE_SIDED, nb.NBODY_PASS_SYMMETRIC
+    V = A + (1 << 20)
+
+    def call(n=10, vel=V, dt=1e-3, steps=3, kind=one, ws=None, wsb=0, pm=A, acc=B):
+        return f(vp(pm), vp(vel), vp(acc), n, 1.0, 1e-4, dt, steps, kind, -1, ws, wsb, None)
+
+    assert call(steps=-1) == INV
+    assert call(dt=float("nan")) == INV
+    assert call(dt=float("inf")) == INV
+    assert call(kind=3) == INV
+    assert call(n=0) == nb.NBODY_OK
+    assert call(steps=0) == nb.NBODY_OK
+    assert call(vel=0) == INV
+    assert call(vel=V + 4) == nb.NBODY_ERR_ALIGNMENT
+    assert call(vel=A) == nb.NBODY_ERR_ALIAS
+    assert call(vel=B + 32) == nb.NBODY_ERR_ALIAS
+    assert call(acc=A) == nb.NBODY_ERR_ALIAS               # the force pass's own checks
+    assert call(kind=sym) == nb.NBODY_ERR_WORKSPACE
+    need = nb.nbody_accel_symmetric_workspace_bytes(10)
+    assert call(kind=sym, ws=vp(C), wsb=need, vel=C + 16) == nb.NBODY_ERR_ALIAS
