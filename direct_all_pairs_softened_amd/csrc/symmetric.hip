@@ -34,15 +34,17 @@
 // Output of a task: panel I's sums from panel J and, for I < J, panel J's
 // sums from panel I, each in its own workspace slot of NC x B floats (NC = 3
 // sums per body, 4 with the potential).  A second kernel forms
-// a_i = G * sum_{J = 0 .. P-1} part[I(i)][J][i], ascending J.
+// a_i = G * sum_{J = 0 .. P-1} part[I(i)][J][i], the J in blocks of 32
+// panels (ascending within a block, block sums ascending).
 // The pass runs either whole (one task launch over all P (P + 1) / 2 panel
 // pairs, slots [P][P]: 12 N^2 / B bytes) or in column chunks: a launch takes
-// the pairs with J in [c0, c1) (SlotMap gives their slots), and the chunk's
-// reduce continues each touched body's fp32 running sum (kept in accel_out
-// between chunks) in ascending J.  A body's panel sums are then added in the
-// same order as in the whole pass, so the two give bitwise equal results; the
-// chunked workspace is one chunk's slots, about 24 N C bytes for chunks of C
-// panels.
+// the pairs with J in [c0, c1) (SlotMap gives their slots; c0 and c1 are
+// multiples of 32, or c1 = P), and the chunk's reduce continues each touched
+// body's fp32 running sum (kept in accel_out between chunks) with that
+// chunk's blocks.  A body's panel sums are then added in the same order as in
+// the whole pass, so the two give bitwise equal results; the chunked
+// workspace is two chunks' slots (consecutive chunks overlap on two queues),
+// about 48 N C bytes for chunks of C panels.
 //
 // Per pair (two interactions) a lane issues 16 FP32 VALU ops and one
 // v_rsq_f32, plus 7 / K DPP moves (rotated) or 3 / K adds (LDS-carried); the
