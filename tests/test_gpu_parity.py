@@ -482,6 +482,45 @@ def test_symmetric_chunked_is_stream_ordered():
     assert np.array_equal(vel.cpu().numpy()[:, :3], ref[0][:, :3])
 
 
+def test_symmetric_chunked_from_several_host_threads():
+    """Four host threads call the chunked pass at once, each on a stream of
+    its own, three times in a row (the binding releases the interpreter lock
+    during the call, so the calls do overlap in the library): the per-device
+    side queue and its events are taken under a lock for a whole call, and
+    every result equals the whole pass bitwise."""
+    import threading
+    n = 20000
+    pms = [workloads.uniform_cube(n, seed=800 + k)[0] for k in range(4)]
+    ref = [sym_accel(p) for p in pms]
+    need = nb.nbody_accel_symmetric_chunked_workspace_bytes(n, -1, 32)
+    ts = [torch.from_numpy(p).to(DEV) for p in pms]
+    outs = [torch.full_like(ts[0], float("nan")) for _ in range(4)]
+    wss = [torch.empty(need, dtype=torch.uint8, device=DEV) for _ in range(4)]
+    streams = [torch.cuda.Stream() for _ in range(4)]      # default priority
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(k):
+        try:
+            torch.cuda.set_device(0)
+            for _ in range(3):
+                nb.nbody_accel_symmetric_chunked(ts[k], 1.0, 1e-4, outs[k], wss[k],
+                                                 chunk_panels=32, stream=streams[k])
+            streams[k].synchronize()
+        except Exception as e:     # reported in the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not errors, errors
+    assert not any(t.is_alive() for t in threads)
+    for k in range(4):
+        assert np.array_equal(outs[k].cpu().numpy(), ref[k]), k
+
+
 # ---------------------------------------------------------------------------
 # One GPU's share of the i side
 # ---------------------------------------------------------------------------
