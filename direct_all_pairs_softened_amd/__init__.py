@@ -90,7 +90,7 @@ def load_library(path: str | None = None):
         "nbody_accel": (c_int, [vp, c_i64, c_f, c_f, vp, vp]),
         "nbody_accel_variant": (c_int, [vp, c_i64, c_f, c_f, vp, c_int, vp]),
         "nbody_accel_variant_count": (c_int, []),
-        "nbody_accel_variant_info": (c_int, [c_int, pint, pint, pint, pint, pint, pint]),
+        "nbody_accel_variant_info": (c_int, [c_int, pint, pint, pint, pint, pint, pint, pint]),
         "nbody_accel_variant_for_n": (c_int, [c_i64]),
         "nbody_accel_potential": (c_int, [vp, c_i64, c_f, c_f, vp, vp]),
         "nbody_energy_from_potential": (c_int, [vp, vp, vp, c_i64, vp, c_sz, vp, vp]),
@@ -221,10 +221,11 @@ def nbody_accel_variant_count() -> int:
 
 
 def nbody_accel_variant_info(v: int) -> dict:
-    vals = [ctypes.c_int() for _ in range(6)]
+    vals = [ctypes.c_int() for _ in range(7)]
     _check(load_library().nbody_accel_variant_info(int(v), *[ctypes.byref(x) for x in vals]),
            "nbody_accel_variant_info")
-    keys = ("bodies_per_lane", "tile", "waves_per_block", "split", "staging", "unroll")
+    keys = ("bodies_per_lane", "tile", "waves_per_block", "split", "staging", "unroll",
+            "lane_groups")
     return {k: x.value for k, x in zip(keys, vals)}
 
 

@@ -101,7 +101,7 @@ int nbody_abi_version(void) { return NBODY_ABI_VERSION; }
 int nbody_accel_variant_count(void) { return nbody::force_variant_count(); }
 
 int nbody_accel_variant_info(int v, int *bodies_per_lane, int *tile, int *waves_per_block,
-                             int *split, int *staging, int *unroll) {
+                             int *split, int *staging, int *unroll, int *lane_groups) {
   const nbody::ForceVariant *fv = nbody::force_variant(v);
   if (!fv) return NBODY_ERR_INVALID_ARG;
   if (bodies_per_lane) *bodies_per_lane = fv->bodies_per_lane;
@@ -110,6 +110,7 @@ int nbody_accel_variant_info(int v, int *bodies_per_lane, int *tile, int *waves_
   if (split) *split = fv->split;
   if (staging) *staging = fv->staging;
   if (unroll) *unroll = fv->unroll;
+  if (lane_groups) *lane_groups = fv->lane_groups;
   return NBODY_OK;
 }
 

@@ -7,6 +7,9 @@
 //    every lane of a wave reads the same LDS address, which the LDS serves as
 //    a broadcast (the CUDA Handbook's shared-memory page makes the same point
 //    for warps);
+//  - a wave may be split into lane groups that take interleaved j-bodies of
+//    each tile (two LDS addresses per read instead of one), so K i-bodies
+//    per lane need fewer i-bodies per block and small n still fills the chip;
 //  - the block may split j over S parts (waves / S waves per part): each part
 //    walks its own contiguous range of tiles and the part sums are added in
 //    ascending part order through LDS at the end.  This keeps small n
@@ -34,15 +37,25 @@ namespace nbody {
 // (two-level like the acceleration; the j = i pair is dropped by an index
 // test, three more VALU ops per pair) and stores Phi_i = -G phi_i in the
 // output's w.
-template <int K, int T, int WAVES, int S, int U, int OCC, class L, bool POT = false>
+//
+// LG > 1 splits each wave into LG lane groups of 64 / LG lanes: lane group g
+// takes the tile's bodies jj with jj % LG == g (LG consecutive float4s per LDS
+// read, so the groups hit different banks), and a wave covers 64 / LG columns
+// of K i-bodies.  A wave then holds K i-bodies per lane with LG times fewer
+// i-bodies per block, which keeps small n filling the chip with K > 1.  The
+// groups' sums are added in ascending g (ds_bpermute) once, after the last
+// tile, before the parts are added.
+template <int K, int T, int WAVES, int S, int U, int OCC, class L, bool POT = false, int LG = 1>
 __global__ __launch_bounds__(WAVES *kWave)
 __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1))) void force_tile_kernel(
     L lay, int n, int i0, int ni, int n_tiles, int tiles_per_part, float G, float eps2) {
   constexpr int GW = WAVES / S;            // i-groups (waves) per part
+  constexpr int CW = kWave / LG;           // i columns per wave
   constexpr int NTHREADS = WAVES * kWave;  // threads per block
   constexpr int LOADS = (S * T) / NTHREADS;
   static_assert(WAVES % S == 0, "waves must be a multiple of the split");
   static_assert((S * T) % NTHREADS == 0, "staged bodies must divide evenly over threads");
+  static_assert(kWave % LG == 0 && T % LG == 0, "lane groups must divide the wave and the tile");
   static_assert(S == 1 || GW * K * (POT ? 4 : 3) * kWave <= 2 * S * T * 4,
                 "one part's sums must fit in the tile buffers");
   __shared__ float4 tile[2][S * T];
@@ -50,14 +63,16 @@ __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1))) void force_tile_kernel(
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int lane = tid % kWave;
+  const int col = lane % CW;
+  const int lg = lane / CW;
   const int part = wave / GW;
   const int grp = wave % GW;
-  const int base = blockIdx.x * (GW * kWave * K) + grp * kWave + lane;
+  const int base = blockIdx.x * (GW * CW * K) + grp * CW + col;
 
   float xi[K], yi[K], zi[K], ax[K], ay[K], az[K], ap[K];
 #pragma unroll
   for (int q = 0; q < K; ++q) {
-    const int i = base + q * GW * kWave;
+    const int i = base + q * GW * CW;
     const float4 b = lay.load(i0 + (i < ni ? i : ni - 1));
     xi[q] = b.x;
     yi[q] = b.y;
@@ -110,12 +125,12 @@ __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1))) void force_tile_kernel(
         pp[q] = 0.0f;
       }
 #pragma unroll U
-      for (int jj = 0; jj < T; ++jj) {
-        const float4 b = tp[jj];
+      for (int jj = 0; jj < T / LG; ++jj) {
+        const float4 b = tp[jj * LG + lg];
 #pragma unroll
         for (int q = 0; q < K; ++q) {
           if constexpr (POT) {
-            const float mp = (j0 + jj == i0 + base + q * GW * kWave) ? 0.0f : b.w;
+            const float mp = (j0 + jj * LG + lg == i0 + base + q * GW * CW) ? 0.0f : b.w;
             pair_accel_pot(b.x, b.y, b.z, b.w, mp, xi[q], yi[q], zi[q], eps2, px[q], py[q],
                            pz[q], pp[q]);
           }
@@ -132,6 +147,26 @@ __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1))) void force_tile_kernel(
       }
     }
     if (more) stash(cur ^ 1);
+  }
+
+  if constexpr (LG > 1) {
+    // lane group 0 adds groups 1 .. LG-1 in ascending order; the other
+    // groups' lanes carry unused values from here on
+#pragma unroll
+    for (int q = 0; q < K; ++q) {
+      float sx = ax[q], sy = ay[q], sz = az[q], sp = ap[q];
+#pragma unroll
+      for (int g = 1; g < LG; ++g) {
+        sx += __shfl(ax[q], col + g * CW);
+        sy += __shfl(ay[q], col + g * CW);
+        sz += __shfl(az[q], col + g * CW);
+        if constexpr (POT) sp += __shfl(ap[q], col + g * CW);
+      }
+      ax[q] = sx;
+      ay[q] = sy;
+      az[q] = sz;
+      ap[q] = sp;
+    }
   }
 
   if constexpr (S > 1) {
@@ -194,10 +229,10 @@ __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1))) void force_tile_kernel(
     }
   }
 
-  if (part == 0) {
+  if (part == 0 && lg == 0) {
 #pragma unroll
     for (int q = 0; q < K; ++q) {
-      const int i = base + q * GW * kWave;
+      const int i = base + q * GW * CW;
       if constexpr (POT) {
         if (i < ni) lay.store4(i, G * ax[q], G * ay[q], G * az[q], -G * ap[q]);
       } else {
@@ -277,39 +312,49 @@ static hipError_t launch_stream(const float *posmass, float *accel, int n, int i
   return hipGetLastError();
 }
 
-template <int K, int T, int WAVES, int S, int U, int OCC, class L, bool POT = false>
+template <int K, int T, int WAVES, int S, int U, int OCC, int LG, class L, bool POT = false>
 static hipError_t launch_tile(const L &lay, int n, int i0, int ni, float G, float eps2,
                               hipStream_t stream) {
   constexpr int GW = WAVES / S;
-  const int per_block = GW * kWave * K;
+  const int per_block = GW * (kWave / LG) * K;
   const int blocks = (ni + per_block - 1) / per_block;
   const int n_tiles = (n + T - 1) / T;
   const int tiles_per_part = (n_tiles + S - 1) / S;
-  hipLaunchKernelGGL((force_tile_kernel<K, T, WAVES, S, U, OCC, L, POT>), dim3(blocks),
+  hipLaunchKernelGGL((force_tile_kernel<K, T, WAVES, S, U, OCC, L, POT, LG>), dim3(blocks),
                      dim3(WAVES * kWave), 0, stream, lay, n, i0, ni, n_tiles, tiles_per_part, G,
                      eps2);
   return hipGetLastError();
 }
 
-// (id, K, T, waves, S, unroll, occupancy target).  Ids are part of the ABI
-// (nbody_accel_variant):
-//  0  the library's choice up to 2e5 bodies: 64 i-bodies per block, j split
-//     16 ways over 16 waves;
-//  1  the choice above: 2 i-bodies per lane, 8-wave blocks in 2 j parts, a
-//     register budget that fits 8 waves per SIMD (1024 blocks at 2^20);
+// (id, K, T, waves, S, unroll, occupancy target, lane groups).  Ids are part
+// of the ABI (nbody_accel_variant):
+//  0  one i-body per lane, 64 i-bodies per block, j split 16 ways over 16
+//     waves (the small-n shape without lane groups);
+//  1  2 i-bodies per lane, 8-wave blocks in 2 j parts, a register budget that
+//     fits 8 waves per SIMD (1024 blocks at 2^20);
 //  2-4  variant 1 with the inner j loop unrolled 1, 2 and 8 times instead of
 //     4: the unroll sweep (the tunable of the CUDA Handbook's Table 14-2);
 //  5  2 i-bodies per lane in 4-wave blocks without a j split: the LDS twin of
-//     the LDS-free variants 6 and 7 (same K, T and j order, so bitwise equal).
+//     the LDS-free variants 6 and 7 (same K, T and j order, so bitwise equal);
+//  8  the library's choice above 32768 bodies: 2 i-bodies per lane in 2
+//     lane groups, 64 i-bodies per 16-wave block, j split 16 ways, tiles of
+//     128;
+//  9  variant 8 with tiles of 64 (a comparison point);
+// 10  the choice up to 32768 bodies: variant 8 with 4 lane groups (32
+//     i-bodies per block, twice the waves).
 // Earlier tilings (1 to 8 i-bodies per lane, tiles of 64 to 512, 4 to 16
-// waves, j splits of 1 to 16) were measured on MI355X and are not kept.
+// waves, j splits of 1 to 16, 1 to 4 lane groups) were measured on MI355X
+// and are not kept.
 #define NBODY_FORCE_VARIANTS(X)  \
-  X(0, 1, 64, 16, 16, 4, 0)      \
-  X(1, 2, 256, 8, 2, 4, 8)       \
-  X(2, 2, 256, 8, 2, 1, 8)       \
-  X(3, 2, 256, 8, 2, 2, 8)       \
-  X(4, 2, 256, 8, 2, 8, 8)       \
-  X(5, 2, 256, 4, 1, 4, 0)
+  X(0, 1, 64, 16, 16, 4, 0, 1)   \
+  X(1, 2, 256, 8, 2, 4, 8, 1)    \
+  X(2, 2, 256, 8, 2, 1, 8, 1)    \
+  X(3, 2, 256, 8, 2, 2, 8, 1)    \
+  X(4, 2, 256, 8, 2, 8, 8, 1)    \
+  X(5, 2, 256, 4, 1, 4, 0, 1)    \
+  X(8, 2, 128, 16, 16, 4, 8, 2)  \
+  X(9, 2, 64, 16, 16, 4, 8, 2)   \
+  X(10, 2, 128, 16, 16, 4, 8, 4)
 
 // LDS-free variants: (id, K, T, waves, mode, occupancy target); mode 0 =
 // scalar loads of j, 1 = vector loads of one address per wave.
@@ -317,38 +362,56 @@ static hipError_t launch_tile(const L &lay, int n, int i0, int ni, float G, floa
   X(6, 2, 256, 4, 0, 0)          \
   X(7, 2, 256, 4, 1, 0)
 
-static const ForceVariant kVariants[] = {
-#define X(id, K, T, W, S, U, OCC) {K, T, W, S, U, 0},
+// Ids run 0 .. force_variant_count() - 1 over both tables.
+const ForceVariant *force_variant(int v) {
+  switch (v) {
+#define X(id, K, T, W, S, U, OCC, LG)                      \
+  case id: {                                               \
+    static const ForceVariant f{K, T, W, S, U, 0, LG};     \
+    return &f;                                             \
+  }
     NBODY_FORCE_VARIANTS(X)
 #undef X
-#define X(id, K, T, W, MODE, OCC) {K, T, W, 1, 4, 1 + MODE},
-        NBODY_STREAM_VARIANTS(X)
+#define X(id, K, T, W, MODE, OCC)                          \
+  case id: {                                               \
+    static const ForceVariant f{K, T, W, 1, 4, 1 + MODE, 1}; \
+    return &f;                                             \
+  }
+    NBODY_STREAM_VARIANTS(X)
 #undef X
-};
-
-int force_variant_count() { return (int)(sizeof(kVariants) / sizeof(kVariants[0])); }
-
-const ForceVariant *force_variant(int v) {
-  return (v >= 0 && v < force_variant_count()) ? &kVariants[v] : nullptr;
+    default:
+      return nullptr;
+  }
 }
 
-// Measured on MI355X (force-pass sweeps over every variant): small and
-// medium n want one body per lane and a 16-way j split, so that every SIMD
-// holds several waves; from a few hundred thousand bodies on, two bodies per
-// lane in 8-wave blocks (two j parts) with a VGPR budget that fits 8 waves
-// per SIMD is fastest.
-int force_variant_for_n(int64_t n) {
-  if (n <= 200000) return 0;  // 64 i per block, j split 16 ways
-  return 1;                   // 512 i per block, j split 2 ways, 8 waves/SIMD
+int force_variant_count() {
+  int count = 0;
+#define X(...) ++count;
+  NBODY_FORCE_VARIANTS(X)
+  NBODY_STREAM_VARIANTS(X)
+#undef X
+  return count;
 }
+
+// Measured on MI355X (force-pass sweeps, variants interleaved on one box,
+// HIP events around each call).  Up to 32768 bodies variant 10 (4 lane
+// groups, 32 i-bodies per block) makes the most waves and is fastest:
+// 17.2 us at 4096 (variant 0: 24.9), 30.1 us at 8192 (45.1), 85.6 us at
+// 16384 (86.7), 183 us at 24576 (232; there 64-body blocks leave half the
+// CUs with one block).  From 32768 on variant 8 (2 lane groups, 64 i-bodies
+// per block) is the fastest or within 1 % of it: 4.60 ms at 131072 (variant
+// 0: 4.73), 268.5 ms at 1,000,003 (variant 1: 279.0), 289.4 ms at 2^20
+// (variant 1: 291.4); variant 1's 512-body blocks fill whole rounds only
+// near powers of two.
+int force_variant_for_n(int64_t n) { return n <= 32768 ? 10 : 8; }
 
 template <class L>
 static hipError_t dispatch(int v, const L &lay, int n, int i0, int ni, float G, float eps2,
                            hipStream_t stream) {
   switch (v) {
-#define X(id, K, T, W, S, U, OCC) \
-  case id:                        \
-    return launch_tile<K, T, W, S, U, OCC>(lay, n, i0, ni, G, eps2, stream);
+#define X(id, K, T, W, S, U, OCC, LG) \
+  case id:                            \
+    return launch_tile<K, T, W, S, U, OCC, LG>(lay, n, i0, ni, G, eps2, stream);
     NBODY_FORCE_VARIANTS(X)
 #undef X
     default:
@@ -358,17 +421,17 @@ static hipError_t dispatch(int v, const L &lay, int n, int i0, int ni, float G, 
 
 // Variants compiled with the potential sum (the ones force_variant_for_n
 // picks).
-#define NBODY_POT_VARIANTS(X) \
-  X(0, 1, 64, 16, 16, 4, 0)   \
-  X(1, 2, 256, 8, 2, 4, 8)
+#define NBODY_POT_VARIANTS(X)   \
+  X(8, 2, 128, 16, 16, 4, 8, 2) \
+  X(10, 2, 128, 16, 16, 4, 8, 4)
 
 hipError_t launch_force_potential(const float *posmass, int n, float G, float eps2,
                                   float *accel, hipStream_t stream) {
   LayoutAos4 lay{reinterpret_cast<const float4 *>(posmass), reinterpret_cast<float4 *>(accel)};
   switch (force_variant_for_n(n)) {
-#define X(id, K, T, W, S, U, OCC) \
-  case id:                        \
-    return launch_tile<K, T, W, S, U, OCC, LayoutAos4, true>(lay, n, 0, n, G, eps2, stream);
+#define X(id, K, T, W, S, U, OCC, LG) \
+  case id:                            \
+    return launch_tile<K, T, W, S, U, OCC, LG, LayoutAos4, true>(lay, n, 0, n, G, eps2, stream);
     NBODY_POT_VARIANTS(X)
 #undef X
     default:

@@ -20,6 +20,7 @@ struct ForceVariant {
   int split;            // S: j-parts per block (waves / S waves per part)
   int unroll;           // unroll of the inner j loop
   int staging;          // 0: LDS tiles; 1: scalar loads of j; 2: vector loads of j
+  int lane_groups;      // LG: lane groups per wave, each taking every LG-th j of a tile
 };
 
 int force_variant_count();

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define NBODY_ABI_VERSION 2
+#define NBODY_ABI_VERSION 3
 
 /* Largest accepted body count (2^30).  Body indices are 32-bit inside the
  * kernels; byte offsets are 64-bit. */
@@ -85,9 +85,11 @@ int nbody_abi_version(void);
  * zero in ascending j with one fused multiply-add per component, and the
  * tile's partial sum is then added to the running sum (two-level summation,
  * which keeps fp32 rounding at ~u*sqrt(n/T) instead of ~u*sqrt(n)).  A
- * variant that splits j over S parts gives each part a contiguous range of
- * tiles and adds the S part sums in ascending part order.  Finally the sum
- * is multiplied by G.
+ * variant with LG lane groups keeps LG such sums per body, group g over the
+ * tile bodies jj with jj % LG == g (ascending jj), and adds them in
+ * ascending g after the last tile.  A variant that splits j over S parts
+ * gives each part a contiguous range of tiles and adds the S part sums in
+ * ascending part order.  Finally the sum is multiplied by G.
  * ------------------------------------------------------------------------- */
 
 /* Accelerations of all n bodies.
@@ -121,15 +123,18 @@ int nbody_accel_variant_count(void);
  * summation chunk), waves per block, j split S, how j-bodies reach the
  * pair step (staging: 0 = LDS tiles read as wavefront broadcasts; 1 =
  * wave-uniform scalar loads into SGPRs; 2 = vector loads of one address per
- * wavefront, i.e. through the caches only), and the unroll factor of the
- * inner j loop (the tunable of the CUDA Handbook's Table 14-2).  Variants
- * with staging != 0 are an ablation of the LDS design and exist for
+ * wavefront, i.e. through the caches only), the unroll factor of the inner
+ * j loop (the tunable of the CUDA Handbook's Table 14-2), and the lane
+ * groups per wave (LG: lane group g takes the tile's bodies jj with
+ * jj % LG == g, and the LG partial sums of a body are added in ascending g
+ * after the last tile; 1 = every lane takes every j).  Variants with
+ * staging != 0 are an ablation of the LDS design and exist for
  * nbody_accel_variant and nbody_accel_range only.  Returns
  * NBODY_ERR_INVALID_ARG for an unknown v; any pointer may be NULL to skip
  * that field. */
 int nbody_accel_variant_info(int v, int *bodies_per_lane, int *tile,
                              int *waves_per_block, int *split, int *staging,
-                             int *unroll);
+                             int *unroll, int *lane_groups);
 
 /* The variant nbody_accel uses for n bodies. */
 int nbody_accel_variant_for_n(int64_t n);

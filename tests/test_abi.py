@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.nbody_abi_version() == 2
+    assert lib.nbody_abi_version() == 3
     for code in (0, -1, -2, -3, -4, -5):
         s = nb.status_string(code)
         assert s and s != "unknown status"
@@ -52,6 +52,9 @@ def test_variant_table(lib):
         assert info["unroll"] in (1, 2, 4, 8)
         assert info["waves_per_block"] % info["split"] == 0
         assert (info["split"] * info["tile"]) % (64 * info["waves_per_block"]) == 0
+        assert info["lane_groups"] in (1, 2, 4)
+        assert info["tile"] % info["lane_groups"] == 0
+        assert info["staging"] == 0 or info["lane_groups"] == 1
     with pytest.raises(nb.NBodyError):
         nb.nbody_accel_variant_info(count)
     for n in (1, 1000, 1024, 16384, 131072, 1 << 20, 1000003, nb.NBODY_MAX_N):
