@@ -50,7 +50,7 @@ EXPORTS = (
     "nbody_leapfrog_step", "nbody_kick", "nbody_kdk_run",
     "nbody_energy", "nbody_energy_workspace_bytes", "nbody_energy_static",
     "nbody_timer_create", "nbody_timer_mark", "nbody_timer_elapsed_ms", "nbody_timer_destroy",
-    "nbody_time_accel",
+    "nbody_time_accel", "nbody_set_launch_block_cap",
 )
 
 # Force passes of nbody_time_accel.
@@ -132,6 +132,7 @@ def load_library(path: str | None = None):
         "nbody_timer_destroy": (c_int, [vp]),
         "nbody_time_accel": (c_int, [vp, c_i64, c_f, c_f, vp, c_int, c_int, vp, c_sz, c_int,
                                      ctypes.POINTER(c_f), ctypes.POINTER(c_f), vp]),
+        "nbody_set_launch_block_cap": (c_int, [c_i64]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -561,6 +562,14 @@ def nbody_time_accel(posmass, G: float, eps2: float, accel_out, pass_kind: int, 
                                            kernel_ms, _stream(stream)),
            "nbody_time_accel")
     return list(pass_ms)[:reps], list(kernel_ms)[:reps]
+
+
+def nbody_set_launch_block_cap(max_blocks: int) -> None:
+    """Caps the blocks per kernel launch for every later call in the process
+    (0 restores HIP's limit), so that small inputs take the split-launch path:
+    a testing aid."""
+    _check(load_library().nbody_set_launch_block_cap(int(max_blocks)),
+           "nbody_set_launch_block_cap")
 
 
 def nbody_energy_static(posmass, vel, G: float, eps2: float, stats_out, stream=None):

@@ -7,12 +7,31 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <vector>
 
 #include "nbody_internal.hpp"
 
 static_assert(NBODY_ENERGY_STATIC_SCRATCH_BYTES == nbody::kEnergyStaticScratchBytes,
               "the header's scratch size must match the library's");
+
+namespace nbody {
+
+namespace {
+std::atomic<long long> g_launch_block_cap{0};
+}  // namespace
+
+long long launch_block_cap(int threads_per_block) {
+  const long long hw = 0xFFFFFFFFLL / threads_per_block;
+  const long long test = g_launch_block_cap.load(std::memory_order_relaxed);
+  return test > 0 && test < hw ? test : hw;
+}
+
+void set_launch_block_cap(long long blocks) {
+  g_launch_block_cap.store(blocks > 0 ? blocks : 0, std::memory_order_relaxed);
+}
+
+}  // namespace nbody
 
 namespace {
 
@@ -674,6 +693,12 @@ int nbody_kdk_run(float *posmass, float *vel, float *accel, int64_t n, float G, 
                     : nbody::launch_kick(vel, accel, 0.5f * dt, ni, st);
   }
   return hip_status(e);
+}
+
+int nbody_set_launch_block_cap(int64_t max_blocks) {
+  if (max_blocks < 0) return NBODY_ERR_INVALID_ARG;
+  nbody::set_launch_block_cap((long long)max_blocks);
+  return NBODY_OK;
 }
 
 }  // extern "C"

@@ -276,10 +276,11 @@ hipError_t launch_energy(const float *posmass, const float *vel, int n, float G,
                      block_out);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const PanelOrder order = panel_order((n + kPairPanel - 1) / kPairPanel);
-  hipLaunchKernelGGL(energy_pairs_kernel, dim3((unsigned)(kXcds * order.per_xcd)),
-                     dim3(kPairW * kWave), 0, stream, pm, n, order, eps2, task_out);
-  e = hipGetLastError();
+  const long long P = (n + kPairPanel - 1) / kPairPanel;
+  e = launch_pair_ranges(P, 0, tasks, kPairW * kWave, [&](const PanelOrder &o, long long b) {
+    hipLaunchKernelGGL(energy_pairs_kernel, dim3((unsigned)b), dim3(kPairW * kWave), 0, stream,
+                       pm, n, o, eps2, task_out);
+  });
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(energy_final_kernel, dim3(1), dim3(kFinalThreads), 0, stream, block_out,
                      blocks, task_out, tasks, (double)G, stats);

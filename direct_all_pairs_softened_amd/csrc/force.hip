@@ -48,7 +48,8 @@ namespace nbody {
 template <int K, int T, int WAVES, int S, int U, int OCC, class L, bool POT = false, int LG = 1>
 __global__ __launch_bounds__(WAVES *kWave)
 __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1))) void force_tile_kernel(
-    L lay, int n, int i0, int ni, int n_tiles, int tiles_per_part, float G, float eps2) {
+    L lay, int n, int i0, int ni, int n_tiles, int tiles_per_part, float G, float eps2,
+    int block0) {
   constexpr int GW = WAVES / S;            // i-groups (waves) per part
   constexpr int CW = kWave / LG;           // i columns per wave
   constexpr int NTHREADS = WAVES * kWave;  // threads per block
@@ -67,7 +68,7 @@ __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1))) void force_tile_kernel(
   const int lg = lane / CW;
   const int part = wave / GW;
   const int grp = wave % GW;
-  const int base = blockIdx.x * (GW * CW * K) + grp * CW + col;
+  const int base = (block0 + (int)blockIdx.x) * (GW * CW * K) + grp * CW + col;
 
   float xi[K], yi[K], zi[K], ax[K], ay[K], az[K], ap[K];
 #pragma unroll
@@ -253,10 +254,10 @@ template <int K, int T, int WAVES, int MODE, int OCC>
 __global__ __launch_bounds__(WAVES *kWave)
 __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1))) void force_stream_kernel(
     const float4 *__restrict__ pm, int n, int i0, int ni, float G, float eps2,
-    float4 *__restrict__ out) {
+    float4 *__restrict__ out, int block0) {
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
-  const int base = blockIdx.x * (WAVES * kWave * K) + wave * kWave + lane;
+  const int base = (block0 + (int)blockIdx.x) * (WAVES * kWave * K) + wave * kWave + lane;
   int zero = 0;
   if constexpr (MODE == 1) asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
   float xi[K], yi[K], zi[K], ax[K], ay[K], az[K];
@@ -306,10 +307,16 @@ static hipError_t launch_stream(const float *posmass, float *accel, int n, int i
                                 float G, float eps2, hipStream_t stream) {
   const int per_block = WAVES * kWave * K;
   const int blocks = (ni + per_block - 1) / per_block;
-  hipLaunchKernelGGL((force_stream_kernel<K, T, WAVES, MODE, OCC>), dim3(blocks),
-                     dim3(WAVES * kWave), 0, stream, reinterpret_cast<const float4 *>(posmass), n,
-                     i0, ni, G, eps2, reinterpret_cast<float4 *>(accel));
-  return hipGetLastError();
+  const int cap = (int)launch_block_cap(WAVES * kWave);
+  for (int b0 = 0; b0 < blocks; b0 += cap) {
+    hipLaunchKernelGGL((force_stream_kernel<K, T, WAVES, MODE, OCC>),
+                       dim3(blocks - b0 < cap ? blocks - b0 : cap), dim3(WAVES * kWave), 0, stream,
+                       reinterpret_cast<const float4 *>(posmass), n, i0, ni, G, eps2,
+                       reinterpret_cast<float4 *>(accel), b0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <int K, int T, int WAVES, int S, int U, int OCC, int LG, class L, bool POT = false>
@@ -320,10 +327,15 @@ static hipError_t launch_tile(const L &lay, int n, int i0, int ni, float G, floa
   const int blocks = (ni + per_block - 1) / per_block;
   const int n_tiles = (n + T - 1) / T;
   const int tiles_per_part = (n_tiles + S - 1) / S;
-  hipLaunchKernelGGL((force_tile_kernel<K, T, WAVES, S, U, OCC, L, POT, LG>), dim3(blocks),
-                     dim3(WAVES * kWave), 0, stream, lay, n, i0, ni, n_tiles, tiles_per_part, G,
-                     eps2);
-  return hipGetLastError();
+  const int cap = (int)launch_block_cap(WAVES * kWave);
+  for (int b0 = 0; b0 < blocks; b0 += cap) {
+    hipLaunchKernelGGL((force_tile_kernel<K, T, WAVES, S, U, OCC, L, POT, LG>),
+                       dim3(blocks - b0 < cap ? blocks - b0 : cap), dim3(WAVES * kWave), 0, stream,
+                       lay, n, i0, ni, n_tiles, tiles_per_part, G, eps2, b0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // (id, K, T, waves, S, unroll, occupancy target, lane groups).  Ids are part

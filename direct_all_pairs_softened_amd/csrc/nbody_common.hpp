@@ -12,6 +12,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "nbody_internal.hpp"
+
 namespace nbody {
 
 constexpr int kWave = 64;  // CDNA wavefront width
@@ -120,6 +122,25 @@ inline PanelOrder panel_order_range(long long P, long long t0, long long t1) {
 
 // Every pair of P panels.
 inline PanelOrder panel_order(long long P) { return panel_order_range(P, 0, P * (P + 1) / 2); }
+
+// The pairs numbered [first, last) of P panels, one block of `threads`
+// threads per pair, in as few launches as launch_block_cap allows:
+// launch(order, blocks) issues one of them.  A block finds its pair from the
+// order alone, so the split leaves every pair's work unchanged.  Returns the
+// first launch error.
+template <class F>
+hipError_t launch_pair_ranges(long long P, long long first, long long last, int threads,
+                              F launch) {
+  long long cap = launch_block_cap(threads) / kXcds * kXcds;
+  if (cap < kXcds) cap = kXcds;
+  for (long long t0 = first; t0 < last; t0 += cap) {
+    const PanelOrder o = panel_order_range(P, t0, t0 + cap < last ? t0 + cap : last);
+    launch(o, kXcds * o.per_xcd);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
 
 // Number of the first pair with J >= c (c a multiple of the tile side, or P).
 __host__ __device__ inline long long first_pair_of_column(long long c) { return c * (c + 1) / 2; }

@@ -12,6 +12,16 @@
 
 namespace nbody {
 
+// HIP counts a launch's size in work-items with 32 bits per grid dimension,
+// so one launch holds at most (2^32 - 1) / threads blocks.  Launchers whose
+// grid can grow past that (one block per panel pair, or 16 to 32 threads
+// per body) split it into several launches of at most launch_block_cap
+// blocks each; every block computes the same thing in any launch, so the
+// split changes no result.  set_launch_block_cap lowers the cap (0 restores
+// the hardware limit): a testing aid that makes small inputs split.
+long long launch_block_cap(int threads_per_block);
+void set_launch_block_cap(long long blocks);
+
 // Force-pass tiling of one compiled variant.
 struct ForceVariant {
   int bodies_per_lane;  // K: i-bodies held in registers by each lane

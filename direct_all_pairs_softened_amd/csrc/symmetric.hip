@@ -758,40 +758,38 @@ size_t symmetric_chunked_workspace_bytes(int64_t n, int v, bool pot, int chunk_p
 static hipError_t launch_tasks_columns(const float *posmass, int n, float eps2, int v, bool pot,
                                        void *workspace, int c0, int c1, hipStream_t stream) {
   const int P = (int)symmetric_panels(n, v, pot);
-  const PanelOrder order =
-      panel_order_range(P, first_pair_of_column(c0), first_pair_of_column(c1));
+  const long long first = first_pair_of_column(c0), last = first_pair_of_column(c1);
   const SlotMap map{c0, c1};
-  const long long blocks = kXcds * order.per_xcd;
   float *part = reinterpret_cast<float *>(workspace);
   const float4 *pm = reinterpret_cast<const float4 *>(posmass);
   if (!pot) {
     switch (v) {
 #define X(id, K, KP, W, OCC, IL, ML, JL)                                                      \
   case id:                                                                                     \
-    hipLaunchKernelGGL((symmetric_task_kernel<K, KP, W, OCC, IL, false, ML, JL>),              \
-                       dim3((unsigned)blocks), dim3(W * kWave), 0, stream, pm, n, order, map,  \
-                       eps2, part);                                                            \
-    break;
+    return launch_pair_ranges(P, first, last, W * kWave, [&](const PanelOrder &o, long long b) { \
+      hipLaunchKernelGGL((symmetric_task_kernel<K, KP, W, OCC, IL, false, ML, JL>),            \
+                         dim3((unsigned)b), dim3(W * kWave), 0, stream, pm, n, o, map, eps2,   \
+                         part);                                                                \
+    });
       NBODY_SYM_VARIANTS(X)
 #undef X
       default:
         return hipErrorInvalidValue;
     }
-  } else {
-    switch (v) {
+  }
+  switch (v) {
 #define X(id, K, KP, W, OCC, ML, JL)                                                          \
   case id:                                                                                     \
-    hipLaunchKernelGGL((symmetric_task_kernel<K, KP, W, OCC, 1, true, ML, JL>),                \
-                       dim3((unsigned)blocks), dim3(W * kWave), 0, stream, pm, n, order, map,  \
-                       eps2, part);                                                            \
-    break;
-      NBODY_SYM_POT_VARIANTS(X)
+    return launch_pair_ranges(P, first, last, W * kWave, [&](const PanelOrder &o, long long b) { \
+      hipLaunchKernelGGL((symmetric_task_kernel<K, KP, W, OCC, 1, true, ML, JL>),              \
+                         dim3((unsigned)b), dim3(W * kWave), 0, stream, pm, n, o, map, eps2,   \
+                         part);                                                                \
+    });
+    NBODY_SYM_POT_VARIANTS(X)
 #undef X
-      default:
-        return hipErrorInvalidValue;
-    }
+    default:
+      return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 // The reduce of the chunk [c0, c1): the bodies of panels below c1.

@@ -508,6 +508,24 @@ int nbody_time_accel(const float *posmass, int64_t n, float G, float eps2,
                      size_t workspace_bytes, int reps, float *pass_ms,
                      float *kernel_ms, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Launch splitting.  HIP counts a launch's size in work-items with 32 bits
+ * per grid dimension.  The passes whose grid can outgrow that (the one-sided
+ * pass, 16 or 32 threads per body; the pair-symmetric and energy passes, one
+ * block per panel pair: from about 1.2e7 bodies for the energy) issue their
+ * blocks in several launches of at most (2^32 - 1) / block-threads blocks.
+ * Every block computes the same thing in any launch, so results are bitwise
+ * those of one launch.
+ *
+ * nbody_set_launch_block_cap lowers that per-launch block count to
+ * max_blocks for every later call in the process (0 restores the hardware
+ * limit), so that small inputs take the split path too: a testing aid, not
+ * a tuning knob.  It is a process-wide setting read at each launch; calls
+ * already enqueued are unaffected.  Returns NBODY_ERR_INVALID_ARG for
+ * max_blocks < 0.
+ * ------------------------------------------------------------------------- */
+int nbody_set_launch_block_cap(int64_t max_blocks);
+
 #ifdef __cplusplus
 }
 #endif

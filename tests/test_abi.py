@@ -446,3 +446,13 @@ def test_kdk_run_validation(lib):
     assert call(kind=sym) == nb.NBODY_ERR_WORKSPACE
     need = nb.nbody_accel_symmetric_workspace_bytes(10)
     assert call(kind=sym, ws=vp(C), wsb=need, vel=C + 16) == nb.NBODY_ERR_ALIAS
+
+
+def test_launch_block_cap_validation(lib):
+    """nbody_set_launch_block_cap takes a non-negative block count (0 restores
+    the hardware limit) and touches no GPU state."""
+    assert lib.nbody_set_launch_block_cap(-1) == nb.NBODY_ERR_INVALID_ARG
+    assert lib.nbody_set_launch_block_cap(5) == nb.NBODY_OK
+    assert lib.nbody_set_launch_block_cap(0) == nb.NBODY_OK
+    with pytest.raises(nb.NBodyError):
+        nb.nbody_set_launch_block_cap(-7)
