@@ -389,6 +389,23 @@ def test_symmetric_default_variant_at_switch_sizes(n):
     assert np.array_equal(a, sym_accel(pm))
 
 
+@pytest.mark.parametrize("n", [32767, 32768, 32769, 40001])
+def test_one_sided_default_variant_at_switch_size(n):
+    """nbody_accel's choice on both sides of its switch (4 lane groups, 32
+    i-bodies per block, up to 32768 bodies; 2 lane groups, 64 per block,
+    above): lognormal masses, every row against the oracle, and a repeat
+    bitwise."""
+    pm, _ = workloads.uniform_cube(n, seed=500 + n % 89, masses="lognormal")
+    v = nb.nbody_accel_variant_for_n(n)
+    assert v == (10 if n <= 32768 else 8)
+    a = gpu_accel(pm)
+    log(f"one-sided n={n} variant {v}")
+    assert np.all(a[:, 3] == 0)
+    assert_parity(a, ref_accel(pm), f"one-sided default n={n}")
+    assert np.array_equal(a, gpu_accel(pm, variant=v))
+    assert np.array_equal(a, gpu_accel(pm))
+
+
 def test_symmetric_collision1m_ragged_sampled():
     w = workloads.WORKLOADS["collision1m"]
     pm, _ = workloads.make("collision1m")
