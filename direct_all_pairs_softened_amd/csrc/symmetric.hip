@@ -696,8 +696,8 @@ int symmetric_variant_count(bool pot) {
 // Measured on MI355X (force-pass sweeps of every variant on Plummer spheres
 // of 8192 to 524288 bodies, each call timed whole: panel pairs and reduce),
 // all with the j-state in LDS: 2 i-bodies per lane in one-wave blocks up to
-// ~21000 bodies (74.9 us at 16384 against 88.5 us for 4 i-bodies and 95.5 us
-// for the one-sided pass; 105.5 against 110.4 us at 20480, 122.1 against
+// ~21000 bodies (74.9 us at 16384 against 88.5 us for 4 i-bodies, and 85 to
+// 96 us for the one-sided pass; 105.5 against 110.4 us at 20480, 122.1 against
 // 112.5 us at 22528), 4 in one-wave blocks up to ~78000 (0.826 against 0.855
 // ms for 4-wave blocks at 65536, 1.038 against 1.045 ms at 73728, 1.289
 // against 1.228 ms at 81920), 4 in 4-wave blocks up to ~3e5 (3.04 against
