@@ -45,6 +45,10 @@ namespace nbody {
 // i-bodies per block, which keeps small n filling the chip with K > 1.  The
 // groups' sums are added in ascending g (ds_bpermute) once, after the last
 // tile, before the parts are added.
+//
+// block0 is the number of the launch's first block: a grid too large for one
+// launch goes out as several, and block b of the grid computes the same rows
+// in any of them.
 template <int K, int T, int WAVES, int S, int U, int OCC, class L, bool POT = false, int LG = 1>
 __global__ __launch_bounds__(WAVES *kWave)
 __attribute__((amdgpu_waves_per_eu(OCC > 0 ? OCC : 1))) void force_tile_kernel(
