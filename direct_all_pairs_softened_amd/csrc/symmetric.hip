@@ -644,7 +644,9 @@ __global__ __launch_bounds__(256) void symmetric_reduce_walk_kernel(
 // Other shapes measured on MI355X and not kept: the rotated carriage with 2
 // j-bodies per lane, 4 to 16 i-bodies per lane, 6 to 8 waves per SIMD, pair
 // interleave widths 2 and 4 (the same as 1 under this register budget), 6 or
-// all 8 i-masses in LDS, 2 i-bodies per lane in 2-wave blocks, several
+// all 8 i-masses in LDS, 2 i-bodies per lane in 2-wave blocks, 8 in 2-wave
+// and one-wave blocks and 4 in 2-wave blocks (2 to 8 % slower than variant 1
+// at 65536 to 262144 bodies, level at 393216), several
 // one-wave tasks packed into one block (no gain), and loading the next
 // sweep's j-bodies one sweep ahead (up to 5 % slower with 4 i-bodies per
 // lane, no gain with 2).
