@@ -456,3 +456,20 @@ def test_launch_block_cap_validation(lib):
     assert lib.nbody_set_launch_block_cap(0) == nb.NBODY_OK
     with pytest.raises(nb.NBodyError):
         nb.nbody_set_launch_block_cap(-7)
+
+
+@pytest.mark.skipif(__import__("shutil").which("gcc") is None, reason="needs gcc")
+def test_plain_c_client(lib, tmp_path):
+    """include/nbody.h compiles as strict C99 (gcc -pedantic -Werror), and a
+    C program linked against libnbody.so gets the documented answers from
+    the calls that need no GPU (tests/abi_c_client.c)."""
+    import subprocess
+    pkg = os.path.dirname(os.path.abspath(nb.__file__))
+    exe = str(tmp_path / "abi_c_client")
+    cmd = ["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+           "-I", os.path.join(ROOT, "include"), os.path.join(ROOT, "tests", "abi_c_client.c"),
+           "-L", pkg, "-lnbody", f"-Wl,-rpath,{pkg}", "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
