@@ -38,10 +38,11 @@
  *    every sum has a fixed order and no atomics are used.  See
  *    NBODY_SUMMATION_ORDER below.
  *  - The library keeps no state beyond two per-GPU resources made on first
- *    use and kept until the process ends: the side stream and events of
+ *    use and kept until the process ends (the side stream and events of
  *    nbody_accel_symmetric_chunked, and the static scratch of
- *    nbody_energy_static.  Calls on different streams may overlap as long
- *    as they do not write memory another call reads.
+ *    nbody_energy_static) and the process-wide testing cap of
+ *    nbody_set_launch_block_cap.  Calls on different streams may overlap as
+ *    long as they do not write memory another call reads.
  */
 #ifndef NBODY_H
 #define NBODY_H
