@@ -180,3 +180,41 @@ def test_cap_is_restored():
         nb.nbody_set_launch_block_cap(0)
     nb.nbody_accel(pm, G, EPS2, out)
     assert np.array_equal(host(out), capped)
+
+
+def test_energy_past_one_launch_at_full_size():
+    """12.6 million bodies make 18.9 million panel pairs of 2048 bodies, more
+    blocks of 256 threads than one launch can hold (2^32 - 1 work-items), so
+    the energy pair pass really goes out as two launches.  Its W must agree
+    with W from the one-sided pass's potentials (nbody_accel_potential, then
+    nbody_energy_from_potential; fp32 sums of 12.6 million terms, so 2e-5),
+    and a repeat must be bitwise: a range launched twice or not at all would
+    move W by about a tenth."""
+    n = 12_600_000
+    pm_np, v_np = workloads.uniform_cube(n, seed=77, masses="lognormal")
+    need = nb.nbody_energy_workspace_bytes(n)
+    pairs = need // 8 - 8 * (-(-n // 256))          # one double per pair after the block sums
+    assert pairs * 256 > 2**32 - 1, pairs
+    print(f"energy at n={n}: {pairs} panel pairs", flush=True)
+    msum = float(pm_np[:, 3].astype(np.float64).sum())
+    pm, vel = torch.from_numpy(pm_np).to(DEV), torch.from_numpy(v_np).to(DEV)
+    del pm_np, v_np
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    st = torch.full((8,), float("nan"), dtype=torch.float64, device=DEV)
+    nb.nbody_energy(pm, vel, G, EPS2, ws, st)
+    direct = host(st)
+    nb.nbody_energy(pm, vel, G, EPS2, ws, st)
+    assert np.array_equal(host(st), direct)
+    acc = torch.empty_like(pm)
+    nb.nbody_accel_potential(pm, G, EPS2, acc)
+    wsp = torch.empty(nb.nbody_energy_from_potential_workspace_bytes(n), dtype=torch.uint8,
+                      device=DEV)
+    stp = torch.full((8,), float("nan"), dtype=torch.float64, device=DEV)
+    nb.nbody_energy_from_potential(pm, vel, acc, wsp, stp)
+    via_potential = host(stp)
+    e = dict(zip(nb.ENERGY_FIELDS, direct))
+    p = dict(zip(nb.ENERGY_FIELDS, via_potential))
+    print(f"  W {e['W']:.12e} direct, {p['W']:.12e} from potentials", flush=True)
+    assert np.isfinite(e["W"]) and e["W"] < 0
+    assert abs(e["W"] - p["W"]) <= 2e-5 * abs(e["W"])
+    assert abs(e["M"] - msum) <= 1e-12 * msum and abs(p["M"] - msum) <= 1e-12 * msum
