@@ -473,3 +473,16 @@ def test_plain_c_client(lib, tmp_path):
     assert r.returncode == 0, r.stderr
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
+
+
+def test_binding_rejects_host_tensors_and_non_tensors():
+    """The binding only marshals device tensors: a host tensor or a numpy
+    array is refused before anything reaches the library (there is no CPU
+    path to fall back on)."""
+    import numpy as np
+    import torch
+    pm = torch.zeros((8, 4), dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        nb.nbody_accel(pm, 1.0, 1e-4, torch.zeros_like(pm))
+    with pytest.raises(TypeError, match="torch tensor"):
+        nb.nbody_accel(np.zeros((8, 4), np.float32), 1.0, 1e-4, np.zeros((8, 4), np.float32))

@@ -103,3 +103,21 @@ def test_timer_brackets_work_on_its_stream():
         assert after.sum().item() == 8.0
     finally:
         t.close()
+
+
+def test_binding_rejects_wrong_dtype_layout_and_rows():
+    """Device tensors of the wrong dtype, a non-contiguous view, a wrong row
+    width or row count are refused by the binding with a clear error, and
+    the output is left untouched."""
+    pm = torch.zeros((64, 4), dtype=torch.float32, device=DEV)
+    out = torch.full((64, 4), 5.0, dtype=torch.float32, device=DEV)
+    with pytest.raises(TypeError, match="float32"):
+        nb.nbody_accel(pm.double(), G, EPS2, out)
+    with pytest.raises(ValueError, match="contiguous"):
+        nb.nbody_accel(torch.zeros((64, 8), device=DEV)[:, ::2], G, EPS2, out)
+    with pytest.raises(ValueError, match="shape"):
+        nb.nbody_accel(torch.zeros((64, 3), device=DEV), G, EPS2, out)
+    with pytest.raises(ValueError, match="rows"):
+        nb.nbody_accel(pm, G, EPS2, out[:32])
+    torch.cuda.synchronize()
+    assert torch.all(out == 5.0)
