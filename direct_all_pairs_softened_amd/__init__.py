@@ -57,6 +57,7 @@ EXPORTS = (
 NBODY_PASS_ONE_SIDED = 0
 NBODY_PASS_SYMMETRIC = 1
 NBODY_PASS_SYMMETRIC_POTENTIAL = 2
+NBODY_PASS_SYMMETRIC_CHUNKED = 3
 
 ENERGY_FIELDS = ("K", "W", "E", "Px", "Py", "Pz", "M")
 

@@ -548,6 +548,30 @@ int not_capturing(hipStream_t stream) {
   return cs == hipStreamCaptureStatusNone ? NBODY_OK : NBODY_ERR_INVALID_ARG;
 }
 
+// The force pass of nbody_time_accel and nbody_kdk_run: checks the pass
+// kind and that pass's own arguments; *v receives the variant it will run.
+int pass_check(const float *posmass, int64_t n, float G, float eps2, const float *accel,
+               int pass, int variant, void *workspace, size_t workspace_bytes, int *v) {
+  switch (pass) {
+    case NBODY_PASS_ONE_SIDED:
+      *v = variant < 0 ? nbody::force_variant_for_n(n) : variant;
+      return force_aos4_check(posmass, n, G, eps2, accel, *v);
+    case NBODY_PASS_SYMMETRIC:
+    case NBODY_PASS_SYMMETRIC_POTENTIAL: {
+      const bool pot = pass == NBODY_PASS_SYMMETRIC_POTENTIAL;
+      *v = sym_variant(variant, n, pot);
+      return sym_check(posmass, n, G, eps2, accel, *v, pot, workspace, workspace_bytes, true,
+                       true);
+    }
+    case NBODY_PASS_SYMMETRIC_CHUNKED:
+      *v = sym_variant(variant, n, false);
+      return sym_check(posmass, n, G, eps2, accel, *v, false, workspace, workspace_bytes, true,
+                       true, NBODY_SYMMETRIC_DEFAULT_CHUNK);
+    default:
+      return NBODY_ERR_INVALID_ARG;
+  }
+}
+
 void destroy_events(std::vector<hipEvent_t> &ev) {
   for (hipEvent_t &e : ev)
     if (e) (void)hipEventDestroy(e);
@@ -610,19 +634,13 @@ int nbody_time_accel(const float *posmass, int64_t n, float G, float eps2, float
                      int pass, int variant, void *workspace, size_t workspace_bytes, int reps,
                      float *pass_ms, float *kernel_ms, void *stream) {
   if (n == 0 || reps < 1 || reps > kMaxTimedReps || !pass_ms) return NBODY_ERR_INVALID_ARG;
-  const bool one_sided = pass == NBODY_PASS_ONE_SIDED;
-  const bool pot = pass == NBODY_PASS_SYMMETRIC_POTENTIAL;
-  if (!one_sided && pass != NBODY_PASS_SYMMETRIC && !pot) return NBODY_ERR_INVALID_ARG;
   int v;
-  if (one_sided) {
-    v = variant < 0 ? nbody::force_variant_for_n(n) : variant;
-    if (int s = force_aos4_check(posmass, n, G, eps2, accel_out, v)) return s;
-  } else {
-    v = sym_variant(variant, n, pot);
-    if (int s = sym_check(posmass, n, G, eps2, accel_out, v, pot, workspace, workspace_bytes,
-                          true, true))
-      return s;
-  }
+  if (int s = pass_check(posmass, n, G, eps2, accel_out, pass, variant, workspace,
+                         workspace_bytes, &v))
+    return s;
+  const bool one_sided = pass == NBODY_PASS_ONE_SIDED;
+  const bool chunked = pass == NBODY_PASS_SYMMETRIC_CHUNKED;
+  const bool pot = pass == NBODY_PASS_SYMMETRIC_POTENTIAL;
   const hipStream_t st = as_stream(stream);
   if (int s = not_capturing(st)) return s;
   // per pass: start, after the dominant kernel, end
@@ -633,12 +651,17 @@ int nbody_time_accel(const float *posmass, int64_t n, float G, float eps2, float
   b.accel4 = accel_out;
   for (int r = 0; r < reps && e == hipSuccess; ++r) {
     e = hipEventRecord(ev[3 * r], st);
-    if (e == hipSuccess)
-      e = one_sided ? nbody::launch_force(v, Layout::Aos4, b, (int)n, 0, (int)n, G, eps2, st)
-                    : nbody::launch_symmetric_tasks(posmass, (int)n, eps2, v, pot, workspace,
-                                                    st);
+    if (e == hipSuccess) {
+      if (one_sided)
+        e = nbody::launch_force(v, Layout::Aos4, b, (int)n, 0, (int)n, G, eps2, st);
+      else if (chunked)
+        e = nbody::launch_symmetric_chunked(posmass, (int)n, G, eps2, accel_out, v, false,
+                                            NBODY_SYMMETRIC_DEFAULT_CHUNK, workspace, st);
+      else
+        e = nbody::launch_symmetric_tasks(posmass, (int)n, eps2, v, pot, workspace, st);
+    }
     if (e == hipSuccess) e = hipEventRecord(ev[3 * r + 1], st);
-    if (e == hipSuccess && !one_sided)
+    if (e == hipSuccess && !one_sided && !chunked)
       e = nbody::launch_symmetric_reduce((int)n, G, accel_out, v, pot, workspace, st);
     if (e == hipSuccess) e = hipEventRecord(ev[3 * r + 2], st);
   }
@@ -656,19 +679,13 @@ int nbody_kdk_run(float *posmass, float *vel, float *accel, int64_t n, float G, 
                   float dt, int steps, int pass, int variant, void *workspace,
                   size_t workspace_bytes, void *stream) {
   if (steps < 0 || !isfinite(dt)) return NBODY_ERR_INVALID_ARG;
-  const bool one_sided = pass == NBODY_PASS_ONE_SIDED;
-  const bool pot = pass == NBODY_PASS_SYMMETRIC_POTENTIAL;
-  if (!one_sided && pass != NBODY_PASS_SYMMETRIC && !pot) return NBODY_ERR_INVALID_ARG;
   int v;
-  if (one_sided) {
-    v = variant < 0 ? nbody::force_variant_for_n(n) : variant;
-    if (int s = force_aos4_check(posmass, n, G, eps2, accel, v)) return s;
-  } else {
-    v = sym_variant(variant, n, pot);
-    if (int s = sym_check(posmass, n, G, eps2, accel, v, pot, workspace, workspace_bytes, true,
-                          true))
-      return s;
-  }
+  if (int s = pass_check(posmass, n, G, eps2, accel, pass, variant, workspace, workspace_bytes,
+                         &v))
+    return s;
+  const bool one_sided = pass == NBODY_PASS_ONE_SIDED;
+  const bool chunked = pass == NBODY_PASS_SYMMETRIC_CHUNKED;
+  const bool pot = pass == NBODY_PASS_SYMMETRIC_POTENTIAL;
   if (n == 0 || steps == 0) return NBODY_OK;
   if (!vel) return NBODY_ERR_INVALID_ARG;
   if (!aligned(vel, 16)) return NBODY_ERR_ALIGNMENT;
@@ -677,6 +694,10 @@ int nbody_kdk_run(float *posmass, float *vel, float *accel, int64_t n, float G, 
       (!one_sided && overlap(vel, bytes, workspace, workspace_bytes)))
     return NBODY_ERR_ALIAS;
   const hipStream_t st = as_stream(stream);
+  // the chunked pass's side stream is shared by every call on the GPU, so a
+  // run that uses it is not captured into a caller's graph
+  if (chunked)
+    if (int s = not_capturing(st)) return s;
   const int ni = (int)n;
   BodyArrays b;
   b.posmass = posmass;
@@ -686,8 +707,13 @@ int nbody_kdk_run(float *posmass, float *vel, float *accel, int64_t n, float G, 
   // the force pass and a closing kick
   hipError_t e = nbody::launch_leapfrog(posmass, vel, accel, dt, ni, st);
   for (int s = 1; s <= steps && e == hipSuccess; ++s) {
-    e = one_sided ? nbody::launch_force(v, Layout::Aos4, b, ni, 0, ni, G, eps2, st)
-                  : nbody::launch_symmetric(posmass, ni, G, eps2, accel, v, pot, workspace, st);
+    if (one_sided)
+      e = nbody::launch_force(v, Layout::Aos4, b, ni, 0, ni, G, eps2, st);
+    else if (chunked)
+      e = nbody::launch_symmetric_chunked(posmass, ni, G, eps2, accel, v, false,
+                                          NBODY_SYMMETRIC_DEFAULT_CHUNK, workspace, st);
+    else
+      e = nbody::launch_symmetric(posmass, ni, G, eps2, accel, v, pot, workspace, st);
     if (e == hipSuccess)
       e = s < steps ? nbody::launch_kick_leapfrog(posmass, vel, accel, dt, ni, st)
                     : nbody::launch_kick(vel, accel, 0.5f * dt, ni, st);

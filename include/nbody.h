@@ -392,13 +392,17 @@ int nbody_kick(float *vel, const float *accel, float h, int64_t n,
  *                 accel.w carries Phi_i on return (it is not read).
  *   pass          one of the NBODY_PASS_* values defined with
  *                 nbody_time_accel below: the one-sided pass
- *                 (nbody_accel_variant), the pair-symmetric pass (whole, not
- *                 chunked) or that pass with the potential; variant -1 for the
- *                 library's choice; workspace as that pass needs (unused
- *                 by the one-sided pass).
+ *                 (nbody_accel_variant), the pair-symmetric pass, that pass
+ *                 with the potential, or the pair-symmetric pass in column
+ *                 chunks of NBODY_SYMMETRIC_DEFAULT_CHUNK panels (bitwise
+ *                 the whole pass's result, in a workspace of about 48 n 32
+ *                 bytes); variant -1 for the library's choice; workspace as
+ *                 that pass needs (unused by the one-sided pass).
  * Like every compute entry point it allocates nothing and does not
  * synchronise, and it records no memset, so a caller may capture it into a
- * HIP graph on a stream of its own and replay it.
+ * HIP graph on a stream of its own and replay it; with
+ * NBODY_PASS_SYMMETRIC_CHUNKED, whose side stream every call on the GPU
+ * shares, a stream being captured is NBODY_ERR_INVALID_ARG instead.
  * steps == 0 or n == 0 is a no-op.  The arrays must be pairwise disjoint
  * and disjoint from the workspace.  Other arguments and errors as the force
  * pass and nbody_leapfrog_step. */
@@ -489,6 +493,7 @@ int nbody_timer_destroy(nbody_timer *timer);
 #define NBODY_PASS_ONE_SIDED 0            /* nbody_accel_variant; -1: nbody_accel */
 #define NBODY_PASS_SYMMETRIC 1            /* nbody_accel_symmetric */
 #define NBODY_PASS_SYMMETRIC_POTENTIAL 2  /* nbody_accel_symmetric_potential */
+#define NBODY_PASS_SYMMETRIC_CHUNKED 3    /* nbody_accel_symmetric_chunked, default chunk */
 
 /* Runs `reps` force passes of the given kind back to back on `stream`, each
  * bracketed by events recorded inside the library, waits for the last, and
@@ -496,11 +501,14 @@ int nbody_timer_destroy(nbody_timer *timer);
  *   pass_ms[r]    duration of pass r (all of its kernels);
  *   kernel_ms[r]  duration of its dominant kernel alone: the panel-pair
  *                 kernel of the pair-symmetric passes (their reduce kernel
- *                 follows it), the whole pass for the one-sided one.  May be
- *                 NULL.
+ *                 follows it), the whole pass for the one-sided one and for
+ *                 the chunked one (whose chunks overlap on two queues).  May
+ *                 be NULL.
  *   variant       as the pass's entry point (-1: the library's choice).
  *   workspace     the pair-symmetric passes' workspace (ignored for the
- *                 one-sided pass; may then be NULL).
+ *                 one-sided pass; may then be NULL); for the chunked pass
+ *                 nbody_accel_symmetric_chunked_workspace_bytes(n, variant,
+ *                 0) bytes.
  * Other arguments, sizes and errors as the pass's entry point; additionally
  * NBODY_ERR_INVALID_ARG for n == 0, reps < 1 or reps > 1 << 16, an unknown
  * pass, a NULL pass_ms, or a stream being captured. */

@@ -349,7 +349,7 @@ def test_timing_validation(lib):
     assert call(n=0) == INV                       # nothing to time
     assert call(reps=0) == INV
     assert call(reps=(1 << 16) + 1) == INV
-    assert call(kind=3) == INV
+    assert call(kind=4) == INV
     assert call(kind=-1) == INV
     assert call(pms=None) == INV
     assert call(eps2=0.0) == INV                  # the pass's own checks
@@ -360,6 +360,11 @@ def test_timing_validation(lib):
     need = nb.nbody_accel_symmetric_workspace_bytes(10)
     assert call(kind=sym, ws=vp(C), wsb=need - 1) == nb.NBODY_ERR_WORKSPACE
     assert call(kind=sym, ws=vp(A), wsb=need) == nb.NBODY_ERR_ALIAS
+    chk = nb.NBODY_PASS_SYMMETRIC_CHUNKED
+    need_c = nb.nbody_accel_symmetric_chunked_workspace_bytes(10, -1, 0)
+    assert call(kind=chk) == nb.NBODY_ERR_WORKSPACE
+    assert call(kind=chk, ws=vp(C), wsb=need_c - 1) == nb.NBODY_ERR_WORKSPACE
+    assert call(kind=chk, ws=vp(B), wsb=need_c) == nb.NBODY_ERR_ALIAS
     t = vp()
     assert lib.nbody_timer_create(0, ctypes.byref(t)) == INV
     assert lib.nbody_timer_create((1 << 20) + 1, ctypes.byref(t)) == INV
@@ -435,7 +440,7 @@ def test_kdk_run_validation(lib):
     assert call(steps=-1) == INV
     assert call(dt=float("nan")) == INV
     assert call(dt=float("inf")) == INV
-    assert call(kind=3) == INV
+    assert call(kind=4) == INV
     assert call(n=0) == nb.NBODY_OK
     assert call(steps=0) == nb.NBODY_OK
     assert call(vel=0) == INV
@@ -446,6 +451,11 @@ def test_kdk_run_validation(lib):
     assert call(kind=sym) == nb.NBODY_ERR_WORKSPACE
     need = nb.nbody_accel_symmetric_workspace_bytes(10)
     assert call(kind=sym, ws=vp(C), wsb=need, vel=C + 16) == nb.NBODY_ERR_ALIAS
+    chk = nb.NBODY_PASS_SYMMETRIC_CHUNKED
+    need_c = nb.nbody_accel_symmetric_chunked_workspace_bytes(10, -1, 0)
+    assert call(kind=chk) == nb.NBODY_ERR_WORKSPACE
+    assert call(kind=chk, ws=vp(C), wsb=need_c - 1) == nb.NBODY_ERR_WORKSPACE
+    assert call(kind=chk, ws=vp(C), wsb=need_c, vel=C + 16) == nb.NBODY_ERR_ALIAS
 
 
 def test_launch_block_cap_validation(lib):

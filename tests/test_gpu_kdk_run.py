@@ -14,7 +14,8 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 G, EPS2, DT = 1.0, 1e-4, 1e-3
-KINDS = [nb.NBODY_PASS_ONE_SIDED, nb.NBODY_PASS_SYMMETRIC, nb.NBODY_PASS_SYMMETRIC_POTENTIAL]
+KINDS = [nb.NBODY_PASS_ONE_SIDED, nb.NBODY_PASS_SYMMETRIC, nb.NBODY_PASS_SYMMETRIC_POTENTIAL,
+         nb.NBODY_PASS_SYMMETRIC_CHUNKED]
 
 
 def workspace(kind, n):
@@ -22,6 +23,8 @@ def workspace(kind, n):
         return None
     if kind == nb.NBODY_PASS_SYMMETRIC:
         need = nb.nbody_accel_symmetric_workspace_bytes(n)
+    elif kind == nb.NBODY_PASS_SYMMETRIC_CHUNKED:
+        need = nb.nbody_accel_symmetric_chunked_workspace_bytes(n, -1, 0)
     else:
         need = nb.nbody_accel_symmetric_potential_workspace_bytes(n)
     return torch.empty(max(need, 16), dtype=torch.uint8, device=DEV)
@@ -32,6 +35,8 @@ def force(kind, pm, acc, ws, stream=None):
         nb.nbody_accel(pm, G, EPS2, acc, stream)
     elif kind == nb.NBODY_PASS_SYMMETRIC:
         nb.nbody_accel_symmetric(pm, G, EPS2, acc, ws, stream=stream)
+    elif kind == nb.NBODY_PASS_SYMMETRIC_CHUNKED:
+        nb.nbody_accel_symmetric_chunked(pm, G, EPS2, acc, ws, stream=stream)
     else:
         nb.nbody_accel_symmetric_potential(pm, G, EPS2, acc, ws, stream=stream)
 
@@ -72,6 +77,24 @@ def test_kdk_run_equals_the_calls_one_by_one(kind, steps):
     s.synchronize()
     for w, g_, name in zip(state(*ref), state(pm, vel, acc), ("posmass", "vel", "accel")):
         assert np.array_equal(w, g_), f"kind {kind} steps {steps}: {name}"
+
+
+def test_kdk_run_chunked_equals_whole_pass():
+    """The step loop through the pass in column chunks (bounded workspace)
+    leaves bitwise the state of the loop through the whole pass: 40000
+    bodies (157 panels of 256), 3 steps of 5 column chunks each."""
+    assert nb.nbody_accel_symmetric_panel(nb.nbody_accel_symmetric_variant_for_n(40000)) == 256
+    n = 40000
+    pm, vel, acc, ws = start(nb.NBODY_PASS_SYMMETRIC, n, seed=61)
+    work = [t.clone() for t in (pm, vel, acc)]
+    wsc = workspace(nb.NBODY_PASS_SYMMETRIC_CHUNKED, n)
+    assert wsc.numel() < ws.numel()
+    torch.cuda.synchronize()
+    nb.nbody_kdk_run(pm, vel, acc, G, EPS2, DT, 3, nb.NBODY_PASS_SYMMETRIC, workspace=ws)
+    nb.nbody_kdk_run(*work, G, EPS2, DT, 3, nb.NBODY_PASS_SYMMETRIC_CHUNKED, workspace=wsc)
+    torch.cuda.synchronize()
+    for w, g_, name in zip(state(pm, vel, acc), state(*work), ("posmass", "vel", "accel")):
+        assert np.array_equal(w, g_), name
 
 
 def test_kdk_run_captured_by_the_caller_and_replayed():

@@ -24,6 +24,8 @@ def plain_pass(kind, pm, ws):
         nb.nbody_accel(pm, G, EPS2, out)
     elif kind == nb.NBODY_PASS_SYMMETRIC:
         nb.nbody_accel_symmetric(pm, G, EPS2, out, ws)
+    elif kind == nb.NBODY_PASS_SYMMETRIC_CHUNKED:
+        nb.nbody_accel_symmetric_chunked(pm, G, EPS2, out, ws)
     else:
         nb.nbody_accel_symmetric_potential(pm, G, EPS2, out, ws)
     torch.cuda.synchronize()
@@ -35,13 +37,16 @@ def workspace(kind):
         return None
     if kind == nb.NBODY_PASS_SYMMETRIC:
         need = nb.nbody_accel_symmetric_workspace_bytes(N)
+    elif kind == nb.NBODY_PASS_SYMMETRIC_CHUNKED:
+        need = nb.nbody_accel_symmetric_chunked_workspace_bytes(N, -1, 0)
     else:
         need = nb.nbody_accel_symmetric_potential_workspace_bytes(N)
     return torch.empty(need, dtype=torch.uint8, device=DEV)
 
 
 @pytest.mark.parametrize("kind", [nb.NBODY_PASS_ONE_SIDED, nb.NBODY_PASS_SYMMETRIC,
-                                  nb.NBODY_PASS_SYMMETRIC_POTENTIAL])
+                                  nb.NBODY_PASS_SYMMETRIC_POTENTIAL,
+                                  nb.NBODY_PASS_SYMMETRIC_CHUNKED])
 def test_time_accel_runs_the_pass(kind):
     pm_np, _ = workloads.uniform_cube(N, seed=910 + kind, masses="lognormal")
     pm = torch.from_numpy(pm_np).to(DEV)
