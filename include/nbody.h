@@ -122,7 +122,8 @@ int nbody_accel_variant_count(void);
 
 /* Describes variant v: bodies per lane, tile width T (the two-level
  * summation chunk), waves per block, j split S, how j-bodies reach the
- * pair step (staging: 0 = LDS tiles read as wavefront broadcasts; 1 =
+ * pair step (staging: 0 = LDS tiles, each read serving a whole wavefront
+ * or, with lane groups, each lane group from one address; 1 =
  * wave-uniform scalar loads into SGPRs; 2 = vector loads of one address per
  * wavefront, i.e. through the caches only), the unroll factor of the inner
  * j loop (the tunable of the CUDA Handbook's Table 14-2), and the lane
